@@ -1,0 +1,532 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch, so
+that the same pins run on the real oracle (``test_oracle_*.py``) and on copies
+of it with planted mistakes (``test_oracle_mutants.py``), where at least one
+pin must fail for every mutant.
+
+What pins what (the pages print no numeric example for this kernel, so the
+pins come from the mathematics and from library routines):
+  binary16 conversions   numpy's own float16 conversions (library routine)
+  quantiser              exact dyadic special case; amax -> +-127; the
+                         half-step rounding bound; ties to even; zero rows;
+                         subnormal scales; bf16 source == its fp32 widening
+  append placement       exactly representable rows land, transposed for V,
+                         at ctx - d + t; nothing else in the pools changes
+  attention              numpy dense brute force (no paging, no quantisation);
+                         T=1 / prefix consistency; shared-prefix pages ==
+                         private copies; page-permutation invariance; closed
+                         forms (q = 0 -> mean of V-hat, one key -> that row)
+  split + merge          the split path merged by the log-sum-exp identity ==
+                         unsplit; merge closed forms (equal weights, one live
+                         split, shift invariance)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle.dense import dense_block_attention
+from speculative_decode_attention_amd import synth
+
+
+# --------------------------------------------------------------------------
+# helpers (plain indexing and widening, no method arithmetic beyond the
+# definitions each pin states)
+# --------------------------------------------------------------------------
+def f16_value(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_value(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_bits_exact(x):
+    """float32 values that are exactly bf16 -> their bit patterns (checks exactness)."""
+    x = np.asarray(x, dtype=np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bf16_value(bits), x.astype(np.float64)), "value not exact in bf16"
+    return bits
+
+
+def dense_from_direct(wl, b):
+    """Dequantised dense context of request b of a direct-value workload."""
+    k, v, ks, vs = wl.direct_tokens[b]
+    k_hat = f16_value(ks)[:, :, None] * k.astype(np.float64)
+    v_hat = f16_value(vs)[:, :, None] * v.astype(np.float64)
+    return k_hat, v_hat
+
+
+def apply_appends(orc, wl):
+    """Pools of a quantised workload after the oracle runs its append phases."""
+    kp, vp, ks, vs = wl.k_pool.copy(), wl.v_pool.copy(), wl.k_scale.copy(), wl.v_scale.copy()
+    for ph in wl.appends:
+        orc.kv_append_int8(ph.k_src, ph.v_src, kp, vp, ks, vs, ph.block_table,
+                           ph.context_lens, ph.draft_lens)
+    return kp, vp, ks, vs
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# binary16
+# --------------------------------------------------------------------------
+def pin_f16_widening_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([orc.f16_to_f32(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _f16_edge_values():
+    vals = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24,
+            2.0 ** -25, 2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -12),
+            6.1e-5, 5.96e-8, 1e-10, 1.0 / 127.0, 3.0 / 127.0, np.inf, -np.inf]
+    # exact ties between neighbouring binary16 values, in normal and subnormal range
+    for e in (-24, -20, -15, -14, -10, -1, 0, 3, 10, 15):
+        for m in (0, 1, 2, 3, 511, 1022):
+            lo = (1024 + m) * 2.0 ** (e - 10) if e >= -14 else m * 2.0 ** -24
+            step = 2.0 ** (e - 10) if e >= -14 else 2.0 ** -24
+            vals.append(lo + step / 2)
+            vals.append(-(lo + step / 2))
+    return np.array(vals, dtype=np.float32)
+
+
+def pin_f32_to_f16_matches_numpy(orc, n_random=40000, seed=7):
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, 2 ** 32, size=n_random, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    mid = (rng.standard_normal(n_random) * np.exp(rng.uniform(-20, 12, n_random))).astype(np.float32)
+    xs = np.concatenate([_f16_edge_values(), rnd, mid])
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(float(x)) for x in xs], dtype=np.uint16)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"binary16 rounding differs for {xs[bad[:5]]}: {got[bad[:5]]} vs {ref[bad[:5]]}"
+
+
+# --------------------------------------------------------------------------
+# quantiser
+# --------------------------------------------------------------------------
+def pin_quant_dyadic(orc, seed=11):
+    """x = k * 2^-5 with integer k, max|k| = 127: scale is exactly 2^-5, codes are k."""
+    rng = np.random.default_rng(seed)
+    for D in (16, 64, 256):
+        k = rng.integers(-127, 128, size=(64, D))
+        k[np.arange(64), rng.integers(0, D, 64)] = rng.choice([-127, 127], size=64)
+        x = (k * 2.0 ** -5).astype(np.float32)
+        q, s = orc.quantize_rows(x)
+        assert np.all(s == np.float16(2.0 ** -5).view(np.uint16))
+        assert np.array_equal(q.astype(np.int64), k)
+
+
+def _random_rows(seed, n=3000, D=256):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    x *= np.exp(rng.uniform(-6, 6, size=(n, 1))).astype(np.float32)
+    return x
+
+
+def pin_quant_amax_maps_to_127(orc, seed=12):
+    x = _random_rows(seed)
+    q, s = orc.quantize_rows(x)
+    i = np.argmax(np.abs(x), axis=1)
+    top = q[np.arange(len(q)), i].astype(np.int64)
+    assert np.array_equal(np.abs(top), np.full(len(q), 127))
+    assert np.array_equal(np.sign(top), np.sign(x[np.arange(len(q)), i]).astype(np.int64))
+
+
+def pin_quant_half_step(orc, seed=13):
+    """Round to nearest with the stored scale: |x - s q| <= s/2 (unclamped)."""
+    x = _random_rows(seed)
+    q, s = orc.quantize_rows(x)
+    sv = f16_value(s)[:, None]
+    # the scale is the binary16 value nearest to the fp32 quotient amax / 127
+    quot = (np.max(np.abs(x), axis=1) / np.float32(127)).astype(np.float64)
+    here = np.abs(f16_value(s) - quot)
+    for nb in (s.astype(np.int64) - 1, s.astype(np.int64) + 1):
+        nb = np.clip(nb, 0, 0x7bff).astype(np.uint16)
+        assert np.all(here <= np.abs(f16_value(nb) - quot))
+    err = np.abs(x.astype(np.float64) - sv * q.astype(np.float64))
+    assert np.all(err <= sv / 2 * (1 + 1e-6))
+    assert q.min() >= -127 and q.max() <= 127
+
+
+def pin_quant_ties_to_even(orc):
+    D = 16
+    m = np.arange(-120, 120)
+    rows = []
+    for i in range(0, len(m), D - 1):
+        chunk = m[i:i + D - 1]
+        vals = (chunk + 0.5) * 2.0 ** -5
+        row = np.concatenate([[127 * 2.0 ** -5], vals, np.zeros(D - 1 - len(chunk))])
+        rows.append(row)
+    x = np.array(rows, dtype=np.float32)
+    q, s = orc.quantize_rows(x)
+    assert np.all(s == np.float16(2.0 ** -5).view(np.uint16))
+    for r, row in enumerate(rows):
+        for d in range(1, D):
+            t = row[d] / 2.0 ** -5
+            if t == 0:
+                continue
+            lo = np.floor(t)
+            want = lo if lo % 2 == 0 else lo + 1
+            assert q[r, d] == want, (t, q[r, d], want)
+
+
+def pin_quant_zero_and_tiny(orc):
+    x = np.zeros((3, 64), dtype=np.float32)
+    x[1, 5] = 1e-9             # amax / 127 underflows binary16 -> scale 0
+    x[2, :] = -0.0
+    q, s = orc.quantize_rows(x)
+    assert np.all(q == 0) and np.all(s == 0)
+
+
+def pin_quant_subnormal_scale(orc, seed=14):
+    """Scales in the binary16 subnormal range: codes stay in [-127, 127], rounding
+    holds where unclamped, clamped codes carry the sign at magnitude 127."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((500, 64)).astype(np.float32)
+    x *= np.exp(rng.uniform(np.log(2e-6), np.log(6e-4), size=(500, 1))).astype(np.float32)
+    q, s = orc.quantize_rows(x)
+    sv = f16_value(s)
+    assert np.any((s > 0) & (s < 0x0400)), "no subnormal scale was exercised"
+    assert q.min() >= -127 and q.max() <= 127
+    for r in np.flatnonzero(sv > 0):
+        t = x[r].astype(np.float64) / sv[r]
+        clamped = np.abs(t) > 127.5
+        assert np.all(q[r][clamped] == np.sign(t[clamped]) * 127)
+        err = np.abs(x[r].astype(np.float64) - sv[r] * q[r].astype(np.float64))
+        assert np.all(err[~clamped] <= sv[r] / 2 * (1 + 1e-6))
+    assert np.any(np.abs(x.astype(np.float64) / np.where(sv > 0, sv, np.inf)[:, None]) > 127.5)
+
+
+def pin_bf16_source_equals_fp32(orc, seed=15):
+    """An append from bf16 rows equals the append of their exact fp32 widening."""
+    wl = synth.make_workload("bf16src", seed, B=2, context_lens=[40, 23], T_max=7, Hq=4, Hkv=2,
+                             D=64, num_pages=32)
+    ph = wl.appends[-1]
+    bits = (ph.k_src.view(np.uint32) >> 16).astype(np.uint16)
+    vbits = (ph.v_src.view(np.uint32) >> 16).astype(np.uint16)
+    widen_k = bf16_value(bits).astype(np.float32)
+    widen_v = bf16_value(vbits).astype(np.float32)
+    pools_a = [a.copy() for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+    pools_b = [a.copy() for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+    orc.kv_append_int8(bits, vbits, *pools_a, ph.block_table, ph.context_lens, ph.draft_lens)
+    orc.kv_append_int8(widen_k, widen_v, *pools_b, ph.block_table, ph.context_lens, ph.draft_lens)
+    for a, b in zip(pools_a, pools_b):
+        assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# append placement
+# --------------------------------------------------------------------------
+def pin_append_placement(orc, seed=16):
+    """Rows k * 2^-5 (codes known without any quantiser) land at ctx - d + t:
+    K at [page][g][slot][:], V transposed at [page][g][:][slot]; nothing else changes."""
+    rng = np.random.default_rng(seed)
+    B, T_max, Hkv, D, P, num_pages = 3, 21, 2, 64, 16, 40
+    ctx = np.array([45, 21, 70], np.int32)
+    dl = np.array([21, 5, 17], np.int32)
+    maxp = 5
+    ids = rng.permutation(num_pages)[:B * maxp].astype(np.int32)
+    bt = ids.reshape(B, maxp)
+    kcodes = rng.integers(-127, 128, size=(B, T_max, Hkv, D))
+    vcodes = rng.integers(-127, 128, size=(B, T_max, Hkv, D))
+    kcodes[..., 0] = 127
+    vcodes[..., 1] = -127
+    ksrc = (kcodes * 2.0 ** -5).astype(np.float32)
+    vsrc = (vcodes * 2.0 ** -5).astype(np.float32)
+    kp, vp, ks, vs = synth.empty_pools(num_pages, Hkv, P, D)
+    kp0, vp0, ks0, vs0 = kp.copy(), vp.copy(), ks.copy(), vs.copy()
+    orc.kv_append_int8(ksrc, vsrc, kp, vp, ks, vs, bt, ctx, dl)
+    touched_k = np.zeros(kp.shape, bool)
+    touched_v = np.zeros(vp.shape, bool)
+    touched_s = np.zeros(ks.shape, bool)
+    s_bits = np.float16(2.0 ** -5).view(np.uint16)
+    for b in range(B):
+        for t in range(dl[b]):
+            pos = ctx[b] - dl[b] + t
+            page, slot = bt[b, pos // P], pos % P
+            for g in range(Hkv):
+                assert np.array_equal(kp[page, g, slot, :].astype(np.int64), kcodes[b, t, g])
+                assert np.array_equal(vp[page, g, :, slot].astype(np.int64), vcodes[b, t, g])
+                assert ks[page, g, slot] == s_bits and vs[page, g, slot] == s_bits
+                touched_k[page, g, slot, :] = True
+                touched_v[page, g, :, slot] = True
+                touched_s[page, g, slot] = True
+    assert np.array_equal(kp[~touched_k], kp0[~touched_k])
+    assert np.array_equal(vp[~touched_v], vp0[~touched_v])
+    assert np.array_equal(ks[~touched_s], ks0[~touched_s])
+    assert np.array_equal(vs[~touched_s], vs0[~touched_s])
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _small_direct(seed, **kw):
+    base = dict(B=2, context_lens=[37, 50], T_max=5, draft_lens=[3, 5], Hq=6, Hkv=2, D=64,
+                num_pages=24, values="direct")
+    base.update(kw)
+    return synth.make_workload("small", seed, **base)
+
+
+def _check_dense(orc, wl, tol):
+    out = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                          wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    for b in range(wl.B):
+        k_hat, v_hat = dense_from_direct(wl, b)
+        d = int(wl.draft_lens[b])
+        if d == 0:
+            assert np.all(np.isnan(out[b]))
+            continue
+        ref = dense_block_attention(bf16_value(wl.q[b, :d]), k_hat, v_hat, wl.sm_scale)
+        assert rel_err(out[b, :d], ref) <= tol, rel_err(out[b, :d], ref)
+        assert np.all(np.isnan(out[b, d:]))     # rows past the draft are never written
+
+
+def pin_attn_dense_exact_values(orc, seed=21):
+    """Dyadic q and power-of-two scales: every score is exact in fp64, so the
+    paged oracle and the dense brute force differ only in summation order."""
+    rng = np.random.default_rng(seed)
+    for (Hq, Hkv, D, P, ctx, dl, T_max) in [(6, 2, 16, 16, [37, 50], [3, 5], 5),
+                                           (8, 2, 64, 16, [256], [4], 4),
+                                           (4, 4, 32, 4, [9, 1, 16], [2, 1, 16], 16)]:
+        wl = synth.make_workload("exact", int(rng.integers(1 << 30)), B=len(ctx), context_lens=ctx,
+                                 T_max=T_max, draft_lens=dl, Hq=Hq, Hkv=Hkv, D=D, P=P,
+                                 num_pages=64, values="direct", sm_scale=1.0 / np.sqrt(D))
+        qv = rng.integers(-8, 9, size=wl.q.shape) * 2.0 ** -3
+        wl.q = bf16_bits_exact(qv.astype(np.float32))
+        for b in range(wl.B):
+            k, v, ks, vs = wl.direct_tokens[b]
+            ks[:] = np.float16(2.0 ** -5).view(np.uint16) * np.ones_like(ks)
+            vs[:] = (np.float16(2.0 ** -4) if b % 2 else np.float16(2.0 ** -6)).view(np.uint16)
+            synth.place_tokens(wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table[b], 0,
+                               k, v, ks, vs)
+        _check_dense(orc, wl, 1e-13)
+
+
+def pin_attn_dense_random(orc, seed=22):
+    """General values (config-1 style draws, several shapes, random placement)."""
+    _check_dense(orc, synth.make_config(1), 1e-12)
+    _check_dense(orc, _small_direct(seed), 1e-12)
+    _check_dense(orc, _small_direct(seed + 1, Hq=12, Hkv=3, D=32, context_lens=[16, 17, 1],
+                                    draft_lens=[16, 0, 1], T_max=16, B=3), 1e-12)
+
+
+def pin_attn_dense_quantized(orc, seed=23):
+    """Quantised workload: pools built by the oracle's appends (paged) against
+    dense K-hat/V-hat from quantising the same source rows token by token."""
+    wl = synth.make_workload("q", seed, B=2, context_lens=[70, 33], T_max=6, draft_lens=[6, 2],
+                             Hq=6, Hkv=2, D=64, num_pages=40, shared_prefix=16)
+    pools = apply_appends(orc, wl)
+    out = orc.verify_attn(wl.q, *pools, wl.block_table, wl.context_lens, wl.draft_lens,
+                          wl.Hkv, wl.sm_scale)
+    # each request's token-major source rows, in position order
+    for b in range(wl.B):
+        rows_k, rows_v = [], []
+        for ph in wl.appends:            # a one-row phase is the shared prefix
+            bb = 0 if ph.block_table.shape[0] == 1 else b
+            n = int(ph.draft_lens[bb])
+            rows_k.append(ph.k_src[bb, :n])
+            rows_v.append(ph.v_src[bb, :n])
+        kx = np.concatenate(rows_k)
+        vx = np.concatenate(rows_v)
+        assert kx.shape[0] == wl.context_lens[b]
+        kq, ksc = orc.quantize_rows(kx)
+        vq, vsc = orc.quantize_rows(vx)
+        k_hat = f16_value(ksc)[:, :, None] * kq.astype(np.float64)
+        v_hat = f16_value(vsc)[:, :, None] * vq.astype(np.float64)
+        d = int(wl.draft_lens[b])
+        ref = dense_block_attention(bf16_value(wl.q[b, :d]), k_hat, v_hat, wl.sm_scale)
+        assert rel_err(out[b, :d], ref) <= 1e-12
+
+
+def pin_attn_prefix_consistency(orc, seed=24):
+    """Row t of a block equals a one-token call at context pos_t + 1 (T=1 is
+    ordinary decode; losslessness against autoregressive decoding)."""
+    wl = _small_direct(seed)
+    full = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                           wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    for b in range(wl.B):
+        for t in range(int(wl.draft_lens[b])):
+            pos = int(wl.context_lens[b] - wl.draft_lens[b] + t)
+            one = orc.verify_attn(np.ascontiguousarray(wl.q[b:b + 1, t:t + 1]), wl.k_pool, wl.v_pool,
+                                  wl.k_scale, wl.v_scale, np.ascontiguousarray(wl.block_table[b:b + 1]),
+                                  np.array([pos + 1], np.int32), np.array([1], np.int32),
+                                  wl.Hkv, wl.sm_scale)
+            assert np.array_equal(one[0, 0], full[b, t])
+    # and T=1 against the dense single-query softmax
+    k_hat, v_hat = dense_from_direct(wl, 0)
+    n = int(wl.context_lens[0])
+    qrow = bf16_value(wl.q[0, :1])
+    one = orc.verify_attn(np.ascontiguousarray(wl.q[:1, :1]), wl.k_pool, wl.v_pool, wl.k_scale,
+                          wl.v_scale, np.ascontiguousarray(wl.block_table[:1]),
+                          np.array([n], np.int32), np.array([1], np.int32), wl.Hkv, wl.sm_scale)
+    ref = dense_block_attention(qrow, k_hat, v_hat, wl.sm_scale)
+    assert rel_err(one[0, :1], ref) <= 1e-12
+
+
+def pin_attn_shared_prefix_equals_private(orc, seed=25):
+    """Requests that share prefix pages give bit-identical rows to requests
+    holding private copies of those pages."""
+    wl = _small_direct(seed, B=3, context_lens=[40, 35, 48], draft_lens=[4, 5, 2], T_max=5,
+                       num_pages=40, shared_prefix=32)
+    shared = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                             wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    kp, vp, ks, vs = wl.k_pool.copy(), wl.v_pool.copy(), wl.k_scale.copy(), wl.v_scale.copy()
+    bt = wl.block_table.copy()
+    free = [p for p in range(wl.num_pages) if p not in set(wl.pages_used.tolist())]
+    for b in range(1, wl.B):
+        for i in range(2):                    # two shared prefix pages
+            src, dst = bt[b, i], free.pop()
+            kp[dst], vp[dst], ks[dst], vs[dst] = kp[src], vp[src], ks[src], vs[src]
+            bt[b, i] = dst
+    assert len(set(bt[:, :2].ravel().tolist())) == 6
+    private = orc.verify_attn(wl.q, kp, vp, ks, vs, bt, wl.context_lens, wl.draft_lens,
+                              wl.Hkv, wl.sm_scale)
+    assert np.array_equal(np.nan_to_num(shared, nan=7.0), np.nan_to_num(private, nan=7.0))
+
+
+def pin_attn_page_permutation(orc, seed=26):
+    wl = _small_direct(seed, num_pages=30)
+    base = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                           wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    perm = np.random.default_rng(seed).permutation(wl.num_pages)   # new id of page p = perm[p]
+    kp, vp, ks, vs = (np.empty_like(a) for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale))
+    kp[perm], vp[perm], ks[perm], vs[perm] = wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale
+    bt = perm[wl.block_table].astype(np.int32)
+    moved = orc.verify_attn(wl.q, kp, vp, ks, vs, bt, wl.context_lens, wl.draft_lens,
+                            wl.Hkv, wl.sm_scale)
+    assert np.array_equal(np.nan_to_num(base, nan=7.0), np.nan_to_num(moved, nan=7.0))
+
+
+def pin_attn_closed_forms(orc, seed=27):
+    wl = _small_direct(seed)
+    # q = 0: every score is 0, the row is the mean of the visible V-hat rows
+    q0 = np.zeros_like(wl.q)
+    out = orc.verify_attn(q0, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                          wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    G = wl.Hq // wl.Hkv
+    for b in range(wl.B):
+        _, v_hat = dense_from_direct(wl, b)
+        for t in range(int(wl.draft_lens[b])):
+            pos = int(wl.context_lens[b] - wl.draft_lens[b] + t)
+            for h in range(wl.Hq):
+                want = v_hat[:pos + 1, h // G].mean(axis=0)
+                assert np.allclose(out[b, t, h], want, rtol=1e-12, atol=1e-14)
+    # a single visible key: the row is that key's V-hat row, exactly
+    one = orc.verify_attn(np.ascontiguousarray(wl.q[:1, :1]), wl.k_pool, wl.v_pool, wl.k_scale,
+                          wl.v_scale, np.ascontiguousarray(wl.block_table[:1]),
+                          np.array([1], np.int32), np.array([1], np.int32), wl.Hkv, wl.sm_scale)
+    _, v_hat = dense_from_direct(wl, 0)
+    for h in range(wl.Hq):
+        assert np.array_equal(one[0, 0, h], v_hat[0, h // G])
+
+
+def pin_rows_api_matches_full(orc, seed=28):
+    wl = _small_direct(seed)
+    full = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                           wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    rows = np.array([(1, 4, 5), (0, 0, 0), (1, 0, 3), (0, 2, 1)], np.int32)
+    got = orc.verify_attn_rows(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                               wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale, rows)
+    for i, (b, t, h) in enumerate(rows):
+        assert np.array_equal(got[i], full[b, t, h])
+
+
+# --------------------------------------------------------------------------
+# split-K and the merge
+# --------------------------------------------------------------------------
+def lse_merge_fp64(part_o, part_lse):
+    """The log-sum-exp identity: softmax over a union of key sets."""
+    M = np.max(part_lse, axis=-1, keepdims=True)
+    w = np.where(np.isneginf(part_lse), 0.0, np.exp(part_lse - np.where(np.isneginf(M), 0, M)))
+    return np.einsum("...s,...sd->...d", w, np.nan_to_num(part_o)) / w.sum(axis=-1)[..., None]
+
+
+def pin_split_equals_unsplit(orc, seed=29):
+    wl = _small_direct(seed, context_lens=[37, 80], draft_lens=[3, 5], num_pages=24)
+    full = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                           wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    for S in (1, 2, 3, 5, 9):
+        po, pl = orc.verify_attn_split(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale,
+                                       wl.block_table, wl.context_lens, wl.draft_lens, wl.Hkv,
+                                       wl.sm_scale, S, wl.max_context_len)
+        merged = lse_merge_fp64(po, pl)                 # [B][Hq][T][D]
+        for b in range(wl.B):
+            d = int(wl.draft_lens[b])
+            got = merged[b, :, :d].transpose(1, 0, 2)
+            assert rel_err(got, full[b, :d]) <= 1e-12, (S, rel_err(got, full[b, :d]))
+        if S == 9:   # more splits than the shorter request has pages: empty splits
+            assert np.any(np.isneginf(pl[0]))
+    # the merge entry point (fp32 partials in, fp64 out) on the split path's output
+    po, pl = orc.verify_attn_split(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale,
+                                   wl.block_table, wl.context_lens, wl.draft_lens, wl.Hkv,
+                                   wl.sm_scale, 4, wl.max_context_len)
+    po32 = np.nan_to_num(po).astype(np.float32)
+    pl32 = np.where(np.isnan(pl), -np.inf, pl).astype(np.float32)
+    out = orc.splitk_merge(po32, pl32, wl.draft_lens, wl.T_max)
+    for b in range(wl.B):
+        d = int(wl.draft_lens[b])
+        assert rel_err(out[b, :d], full[b, :d]) <= 1e-5
+
+
+def pin_merge_closed_forms(orc, seed=30):
+    rng = np.random.default_rng(seed)
+    B, Hq, T, S, D = 2, 3, 4, 5, 8
+    po = rng.standard_normal((B, Hq, T, S, D)).astype(np.float32)
+    dl = np.array([4, 2], np.int32)
+    # equal log-sum-exps: the plain mean of the partial rows
+    pl = np.full((B, Hq, T, S), 1.25, np.float32)
+    out = orc.splitk_merge(po, pl, dl, T)
+    want = po.astype(np.float64).mean(axis=3).transpose(0, 2, 1, 3)
+    assert np.allclose(out[0], want[0], rtol=1e-12, atol=1e-12)
+    assert np.allclose(out[1, :2], want[1, :2], rtol=1e-12, atol=1e-12)
+    assert np.all(np.isnan(out[1, 2:]))                 # rows past the draft untouched
+    # one live split, others empty: exactly that split's row
+    pl = np.full((B, Hq, T, S), -np.inf, np.float32)
+    pl[..., 3] = -2.0
+    out = orc.splitk_merge(po, pl, dl, T)
+    assert np.array_equal(out[0], po[0, :, :, 3].astype(np.float64).transpose(1, 0, 2))
+    # shift invariance and the two-split weights e^a / (e^a + e^b)
+    pl = rng.standard_normal((B, Hq, T, S)).astype(np.float32)
+    a = orc.splitk_merge(po, pl, dl, T)
+    b = orc.splitk_merge(po, (pl + np.float32(3.0)).astype(np.float32), dl, T)
+    assert np.allclose(a[0], b[0], rtol=1e-6, atol=1e-7)
+    pl2 = np.full((B, Hq, T, 2), -np.inf, np.float32)
+    pl2[..., 0], pl2[..., 1] = 0.0, np.log(3.0)
+    po2 = np.ascontiguousarray(po[..., :2, :])
+    out = orc.splitk_merge(po2, pl2, dl, T)
+    want = (0.25 * po2[..., 0, :].astype(np.float64) + 0.75 * po2[..., 1, :]).transpose(0, 2, 1, 3)
+    assert np.allclose(out[0], want[0], rtol=1e-6, atol=1e-7)
+
+
+ALL_PINS = [
+    pin_f16_widening_exhaustive,
+    pin_f32_to_f16_matches_numpy,
+    pin_quant_dyadic,
+    pin_quant_amax_maps_to_127,
+    pin_quant_half_step,
+    pin_quant_ties_to_even,
+    pin_quant_zero_and_tiny,
+    pin_quant_subnormal_scale,
+    pin_bf16_source_equals_fp32,
+    pin_append_placement,
+    pin_attn_dense_exact_values,
+    pin_attn_dense_random,
+    pin_attn_dense_quantized,
+    pin_attn_prefix_consistency,
+    pin_attn_shared_prefix_equals_private,
+    pin_attn_page_permutation,
+    pin_attn_closed_forms,
+    pin_rows_api_matches_full,
+    pin_split_equals_unsplit,
+    pin_merge_closed_forms,
+]
