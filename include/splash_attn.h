@@ -1,0 +1,198 @@
+/*
+ * splash_attn.h -- C ABI of the block-verify decode attention library for
+ * MI355X (gfx950): speculative-decoding verify attention over a paged KV cache
+ * held as int8 codes with one fp16 scale per (token, kv head).
+ *
+ * What the method computes (the pages describe Splash, an inference engine):
+ *  - A draft model proposes a block of tokens and the target model checks the
+ *    whole block in one forward pass (Splash community summary on
+ *    discuss.pytorch.kr, section "DFlash 2 speculative decoding as the default
+ *    path"; bnskd.com article, "Tech core 1").  In attention this is: each of a
+ *    request's d drafted rows attends causally over the cached context and the
+ *    drafts up to and including itself.
+ *  - The decode kernel reads the 8-bit KV cache directly and reuses every page
+ *    across the query heads that share it and across the verify tokens
+ *    (discuss.pytorch.kr summary, section "Metal kernels generated to shape";
+ *    bnskd.com, "Tech core 2").
+ *  - The cache is paged and indexed by prefix: requests with a common prefix
+ *    reuse its pages (discuss.pytorch.kr summary, section "Batch scheduling and
+ *    a memory budget fixed at start-up").  Here that is identical block_table
+ *    entries.
+ *  - Each request in a batch carries its own draft (same summary, DFlash 2
+ *    section), so draft lengths are per request.
+ *  - A decode step is submitted as one unit (same section), so no call here
+ *    synchronises the host; memory is budgeted once at start-up (batching
+ *    section), so no call allocates: the caller owns every buffer.
+ *  - Kernels exist for exact shapes and ship precompiled with presets keyed by
+ *    GPU core count, with no fallback path (summary, Metal-kernels and design
+ *    sections): shapes outside the compiled set return SPLASH_ERR_UNSUPPORTED,
+ *    and num_splits = 0 picks a preset from the device's compute-unit count.
+ *
+ * Conventions for every entry point:
+ *  - Every buffer pointer is a DEVICE pointer owned by the caller.  bf16 and
+ *    fp16 values travel as raw uint16_t bit patterns.  `stream` is a
+ *    hipStream_t passed as void* (NULL = the default stream).
+ *  - Calls only enqueue work on `stream`; they never synchronise and never
+ *    allocate, and keep no per-call state.
+ *  - Argument faults the host can see are returned synchronously as a status
+ *    code and nothing is launched.  Values that live in device memory
+ *    (context_lens, draft_lens, block_table entries) are trusted
+ *    preconditions; violating them is undefined behaviour:
+ *      0 <= draft_lens[b] <= T_max,  draft_lens[b] <= context_lens[b]
+ *      context_lens[b] <= max_context_len (verify)
+ *      ceil(context_lens[b] / P) <= max_pages_per_seq
+ *      every block_table entry that is used lies in [0, num_pages)
+ *      appended positions never land in a page another request shares
+ *  - Layouts (row-major, innermost last):
+ *      q, out       bf16  [B][T_max][Hq][D]
+ *      k_pool       int8  [num_pages][Hkv][P][D]   (a page is P token rows)
+ *      v_pool       int8  [num_pages][Hkv][D][P]   (a page is stored d-major)
+ *      k_scale,
+ *      v_scale      fp16  [num_pages][Hkv][P]
+ *      block_table  int32 [B][max_pages_per_seq]
+ *      context_lens int32 [B]   tokens in the cache AFTER the draft block
+ *      draft_lens   int32 [B]   draft t of request b is at position
+ *                               context_lens[b] - draft_lens[b] + t
+ *    Query head h reads kv head h / (Hq / Hkv).
+ *  - Compiled shapes: P = 16; (D, Hq/Hkv) in {(64, 4), (128, 8), (256, 6)};
+ *    T_max <= 16 for verify.  Append accepts D in {64, 128, 256} and any T_max.
+ *  - q, out, k_pool, v_pool and the workspace must be 16-byte aligned.
+ */
+#ifndef SPLASH_ATTN_H
+#define SPLASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SPLASH_OK = 0,
+    SPLASH_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad ratio, misalignment */
+    SPLASH_ERR_UNSUPPORTED = 2,        /* shape outside the compiled set                     */
+    SPLASH_ERR_WORKSPACE_TOO_SMALL = 3,
+    SPLASH_ERR_LAUNCH = 4,             /* the HIP runtime refused a launch                   */
+    SPLASH_ERR_DEVICE = 5              /* no usable device / device query failed             */
+};
+
+enum { SPLASH_SRC_F32 = 0, SPLASH_SRC_BF16 = 1 };
+
+/*
+ * splash_kv_append_int8 -- quantise new K and V rows into the int8 pools.
+ * The write side of the 8-bit cache (the pages state only that the cache is
+ * 8-bit -- summary, Metal-kernels section -- and that its precision is a
+ * setting -- localai.co.kr 1.3.0 guide).  For each request b, token
+ * t < draft_lens[b] and kv head g, the D source values x (fp32, or bf16
+ * widened exactly) become
+ *     amax  = max_d |x_d|                         (fp32)
+ *     s16   = binary16 nearest to amax / 127      (fp32 division, ties to even)
+ *     code  = clamp(rint(x_d / s), -127, 127)     (s = s16 widened; fp32; 0 if s == 0)
+ * stored at position pos = context_lens[b] - draft_lens[b] + t:
+ *     k_pool[page][g][pos % P][:], v_pool[page][g][:][pos % P],
+ *     k_scale/v_scale[page][g][pos % P], page = block_table[b][pos / P].
+ * Nothing else in the pools changes.  k_new, v_new: [B][T_max][Hkv][D], fp32
+ * (src_dtype SPLASH_SRC_F32) or bf16 (SPLASH_SRC_BF16).  T_max is unbounded, so
+ * one call can also fill a whole context.  Results are bit-exact, reproducible.
+ */
+int splash_kv_append_int8(const void* k_new, const void* v_new, int src_dtype,
+                          int8_t* k_pool, int8_t* v_pool,
+                          uint16_t* k_scale, uint16_t* v_scale,
+                          const int32_t* block_table, int max_pages_per_seq,
+                          const int32_t* context_lens, const int32_t* draft_lens,
+                          int B, int T_max, int Hkv, int D, int P, int num_pages,
+                          void* stream);
+
+/*
+ * splash_verify_attn_default_splits -- the split-K preset: how many context
+ * splits one request's pages are cut into so that B * Hkv * splits work items
+ * fill the device's compute units (presets keyed by core count, as the
+ * summary's Metal-kernels section describes).  Returns >= 1, or a negative
+ * status on bad arguments or a failed device query.
+ */
+int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P, int D);
+
+/*
+ * splash_verify_attn_workspace_bytes -- bytes of device workspace
+ * splash_verify_attn needs for num_splits splits (0 when num_splits <= 1):
+ * fp32 partial rows [B][Hq][T_max][S][D] followed, at a 256-byte aligned
+ * offset, by fp32 log-sum-exps [B][Hq][T_max][S].
+ */
+size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits);
+
+/*
+ * splash_verify_attn -- block-verify attention.  For request b, draft
+ * t < draft_lens[b], query head h (kv head g = h / (Hq/Hkv)), with
+ * pos_t = context_lens[b] - draft_lens[b] + t:
+ *     z_j  = sm_scale * sum_d q[b][t][h][d] * k_scale_j * k_code_j[d],  j = 0..pos_t
+ *     out[b][t][h][:] = bf16( sum_j e^(z_j - max z) v_scale_j v_code_j[:] / sum_j e^(z_j - max z) )
+ * with the codes and scales of token j read through block_table.  Rows
+ * t >= draft_lens[b] of out are left untouched (draft_lens[b] = 0 makes request
+ * b a no-op).  Every page of a (request, kv head) is read from memory once and
+ * serves all Hq/Hkv query heads and all drafts of the request.
+ * max_context_len: host-side upper bound on context_lens (sizes the grid).
+ * num_splits: 0 = preset; > 0 forces that many context splits.  When more than
+ * one split runs, workspace must hold splash_verify_attn_workspace_bytes(...)
+ * bytes (workspace may be NULL when one split runs).  Accumulation is in fp32;
+ * the result is deterministic for a given num_splits.
+ */
+int splash_verify_attn(const uint16_t* q, uint16_t* out,
+                       const int8_t* k_pool, const int8_t* v_pool,
+                       const uint16_t* k_scale, const uint16_t* v_scale,
+                       const int32_t* block_table, int max_pages_per_seq,
+                       const int32_t* context_lens, const int32_t* draft_lens,
+                       int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                       int max_context_len, float sm_scale, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * splash_verify_attn_partition -- the first half of splash_verify_attn on its
+ * own: for each context split s (pages [s*L, (s+1)*L) with
+ * L = splash_verify_attn_split_pages(...)), write the normalised partial row
+ *     part_o[b][h][t][s][:]  = sum_{j in split, j <= pos_t} e^(z_j - m_s) v_hat_j / l_s   (fp32)
+ *     part_lse[b][h][t][s]   = m_s + ln l_s   (natural log; -inf and a zero row
+ *                                             when the split holds no visible key)
+ * for t < draft_lens[b].  For callers that combine partials themselves (for
+ * example across devices) with splash_verify_attn_splitk_merge.  num_splits
+ * must be >= 1 (no preset here); the buffers use exactly num_splits as S.
+ */
+int splash_verify_attn_partition(const uint16_t* q,
+                                 const int8_t* k_pool, const int8_t* v_pool,
+                                 const uint16_t* k_scale, const uint16_t* v_scale,
+                                 const int32_t* block_table, int max_pages_per_seq,
+                                 const int32_t* context_lens, const int32_t* draft_lens,
+                                 int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                                 int max_context_len, float sm_scale, int num_splits,
+                                 float* part_o, float* part_lse, void* stream);
+
+/*
+ * splash_verify_attn_split_pages -- pages per split L that the partition uses
+ * for num_splits splits of a max_context_len context (a multiple of the
+ * kernel's page group), and so the number of splits that hold any page:
+ * ceil(ceil(max_context_len / P) / L).  Negative status on bad arguments.
+ */
+int splash_verify_attn_split_pages(int max_context_len, int P, int num_splits);
+
+/*
+ * splash_verify_attn_splitk_merge -- combine S context splits by their
+ * log-sum-exps: for t < draft_lens[b],
+ *     M = max_s part_lse[b][h][t][s],  w_s = e^(part_lse[b][h][t][s] - M)
+ *     out[b][t][h][:] = bf16( sum_s w_s part_o[b][h][t][s][:] / sum_s w_s )
+ * summed in ascending s (deterministic); splits with lse = -inf weigh nothing
+ * and their rows are not read.  part_o fp32 [B][Hq][T_max][S][D], part_lse fp32
+ * [B][Hq][T_max][S].  Rows t >= draft_lens[b] of out are left untouched.
+ */
+int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse,
+                                    uint16_t* out, const int32_t* draft_lens,
+                                    int B, int T_max, int Hq, int D, int num_splits,
+                                    void* stream);
+
+/* Text for a status code (static storage, never NULL). */
+const char* splash_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLASH_ATTN_H */

@@ -146,8 +146,9 @@ class Oracle:
         return out
 
     def verify_attn_split(self, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
-                          draft_lens, Hkv, sm_scale, num_splits, max_context_len):
-        """-> (part_o fp64 [B][Hq][T_max][S][D], part_lse fp64 [B][Hq][T_max][S])."""
+                          draft_lens, Hkv, sm_scale, num_splits, pages_per_split):
+        """Splits of pages_per_split pages -> (part_o fp64 [B][Hq][T_max][S][D],
+        part_lse fp64 [B][Hq][T_max][S])."""
         B, T_max, Hq, D = q.shape
         num_pages, _, P, _ = k_pool.shape
         S = num_splits
@@ -157,7 +158,7 @@ class Oracle:
             self._ptr(q), self._ptr(k_pool), self._ptr(v_pool), self._ptr(k_scale),
             self._ptr(v_scale), self._ptr(block_table), block_table.shape[1],
             self._ptr(context_lens), self._ptr(draft_lens), B, T_max, Hq, Hkv, D, P, num_pages,
-            float(sm_scale), S, int(max_context_len), self._ptr(part_o), self._ptr(part_lse))
+            float(sm_scale), S, int(pages_per_split), self._ptr(part_o), self._ptr(part_lse))
         if rc:
             raise ValueError(f"oracle verify_attn_split rejected its arguments (rc={rc})")
         return part_o, part_lse

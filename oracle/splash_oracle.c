@@ -36,8 +36,9 @@
  *  - context_lens[b] counts the tokens after the draft block was appended;
  *    draft t sits at position context_lens[b] - draft_lens[b] + t;
  *  - query head h belongs to kv head h / (Hq / Hkv);
- *  - K pool layout [num_pages][Hkv][P][D], V pool layout [num_pages][Hkv][D][P]
- *    (V is stored d-major inside a page), scales [num_pages][Hkv][P];
+ *  - K pool layout [num_pages][Hkv][P][D]; V pool layout
+ *    [num_pages][Hkv][P/8][D][8] (a V page is two d-major tiles of 8 tokens);
+ *    scales [num_pages][Hkv][P]; P must be a multiple of 8;
  *  - q and out are [B][T_max][Hq][D]; rows t >= draft_lens[b] are neither
  *    read nor written.
  *
@@ -143,7 +144,7 @@ void ref_quantize_row(const float* x, int D, int8_t* q, uint16_t* scale16)
 static size_t k_index(int page, int g, int slot, int d, int Hkv, int P, int D)
 { return (((size_t)page * Hkv + g) * P + slot) * D + d; }
 static size_t v_index(int page, int g, int slot, int d, int Hkv, int P, int D)
-{ return (((size_t)page * Hkv + g) * D + d) * P + slot; }
+{ return ((((size_t)page * Hkv + g) * (P / 8) + slot / 8) * D + d) * 8 + slot % 8; }
 static size_t s_index(int page, int g, int slot, int Hkv, int P)
 { return ((size_t)page * Hkv + g) * P + slot; }
 
@@ -163,7 +164,7 @@ int splash_ref_kv_append_int8(const void* k_new, const void* v_new, int src_dtyp
 {
     if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale ||
         !block_table || !context_lens || !draft_lens) return REF_ERR_ARG;
-    if (B < 0 || T_max < 0 || Hkv <= 0 || D <= 0 || P <= 0 || num_pages <= 0 ||
+    if (B < 0 || T_max < 0 || Hkv <= 0 || D <= 0 || P <= 0 || P % 8 != 0 || num_pages <= 0 ||
         (src_dtype != 0 && src_dtype != 1)) return REF_ERR_ARG;
     float row[1024];
     int8_t codes[1024];
@@ -261,7 +262,7 @@ static int check_attn_args(const void* q, const void* out, const void* k_pool, c
     if (!q || !out || !k_pool || !v_pool || !k_scale || !v_scale || !bt ||
         !context_lens || !draft_lens) return REF_ERR_ARG;
     if (B < 0 || T_max < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || P <= 0 ||
-        num_pages <= 0 || max_pages_per_seq < 0) return REF_ERR_ARG;
+        P % 8 != 0 || num_pages <= 0 || max_pages_per_seq < 0) return REF_ERR_ARG;
     for (int b = 0; b < B; ++b) {
         int n = context_lens[b], dl = draft_lens[b];
         if (dl < 0 || dl > T_max || dl > n) return REF_ERR_ARG;
@@ -361,7 +362,7 @@ int splash_ref_verify_attn_rows(const uint16_t* q,
 
 /*
  * splash_ref_verify_attn_split: the same attention evaluated through explicit
- * context splits [s*L*P, (s+1)*L*P) with L = ceil(ceil(max_ctx / P) / S) pages,
+ * context splits [s*L*P, (s+1)*L*P) of L = pages_per_split pages each,
  * giving per split the normalised partial row o_s and its natural-log
  * log-sum-exp lse_s (-inf and a zero row for a split with no visible key).
  * part_o is fp64 [B][Hq][T_max][S][D], part_lse fp64 [B][Hq][T_max][S].
@@ -372,18 +373,16 @@ int splash_ref_verify_attn_split(const uint16_t* q,
                                  const int32_t* block_table, int max_pages_per_seq,
                                  const int32_t* context_lens, const int32_t* draft_lens,
                                  int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
-                                 double sm_scale, int num_splits, int max_context_len,
+                                 double sm_scale, int num_splits, int pages_per_split,
                                  double* part_o, double* part_lse)
 {
     int rc = check_attn_args(q, part_o, k_pool, v_pool, k_scale, v_scale, block_table,
                              context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages,
                              max_pages_per_seq);
     if (rc) return rc;
-    if (num_splits <= 0 || !part_lse) return REF_ERR_ARG;
+    if (num_splits <= 0 || pages_per_split <= 0 || !part_lse) return REF_ERR_ARG;
     int S = num_splits;
-    int max_pages = (max_context_len + P - 1) / P;
-    int L = (max_pages + S - 1) / S;
-    if (L < 1) L = 1;
+    int L = pages_per_split;
     int group = Hq / Hkv;
     int maxn = 0;
     for (int b = 0; b < B; ++b) if (context_lens[b] > maxn) maxn = context_lens[b];

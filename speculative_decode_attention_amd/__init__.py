@@ -1,1 +1,273 @@
-"""Block-verify decode attention over an int8 paged KV cache, for MI355X (gfx950)."""
+"""Block-verify decode attention over an int8 paged KV cache, for MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/splash_attn.h``
+(``libsplash_attn.so``, built from ``csrc/`` by ``build.py``).  Every function
+has the name of the C entry point it calls and only marshals arguments: it
+checks dtypes, devices and shapes of the torch tensors, passes their device
+pointers and the current HIP stream, and raises ``SplashError`` on a non-zero
+status.  All computation happens in the library's kernels; there is no other
+code path, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libsplash_attn.so"
+
+SPLASH_OK = 0
+SPLASH_ERR_INVALID_ARGUMENT = 1
+SPLASH_ERR_UNSUPPORTED = 2
+SPLASH_ERR_WORKSPACE_TOO_SMALL = 3
+SPLASH_ERR_LAUNCH = 4
+SPLASH_ERR_DEVICE = 5
+SPLASH_SRC_F32 = 0
+SPLASH_SRC_BF16 = 1
+PAGE_SIZE = 16
+
+# every symbol the header declares
+EXPORTED = (
+    "splash_kv_append_int8",
+    "splash_verify_attn_default_splits",
+    "splash_verify_attn_workspace_bytes",
+    "splash_verify_attn",
+    "splash_verify_attn_partition",
+    "splash_verify_attn_split_pages",
+    "splash_verify_attn_splitk_merge",
+    "splash_status_string",
+)
+
+
+class SplashError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {splash_status_string(status)} (status {status})")
+
+
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib_handle = None
+
+
+def load_library(path: Path | None = None):
+    """dlopen the library (no GPU is touched) and declare its signatures."""
+    global _lib_handle
+    if path is None and _lib_handle is not None:
+        return _lib_handle
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is not built: run `python -m speculative_decode_attention_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    lib.splash_kv_append_int8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P,
+                                          _I, _I, _I, _I, _I, _I, _P]
+    lib.splash_verify_attn_default_splits.argtypes = [_I, _I, _I, _I, _I]
+    lib.splash_verify_attn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+    lib.splash_verify_attn_workspace_bytes.restype = _Z
+    lib.splash_verify_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                       _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_verify_attn_partition.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                                 _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
+    lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
+    lib.splash_verify_attn_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+    lib.splash_status_string.argtypes = [_I]
+    lib.splash_status_string.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("splash_verify_attn_workspace_bytes", "splash_status_string"):
+            getattr(lib, name).restype = _I
+    if path is None:
+        _lib_handle = lib
+    return lib
+
+
+def _lib():
+    return load_library()
+
+
+def splash_status_string(status: int) -> str:
+    return _lib().splash_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# argument marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(rc, where):
+    if rc != SPLASH_OK:
+        raise SplashError(rc, where)
+
+
+def _pool_dims(k_pool, v_pool, k_scale, v_scale):
+    torch = _torch()
+    if k_pool.dim() != 4:
+        raise ValueError("k_pool must be [num_pages][Hkv][P][D]")
+    num_pages, Hkv, P, D = k_pool.shape
+    _dev(k_pool, "k_pool", (torch.int8,))
+    _dev(v_pool, "v_pool", (torch.int8,), (num_pages, Hkv, P // 8, D, 8))
+    _dev(k_scale, "k_scale", (torch.float16, torch.int16), (num_pages, Hkv, P))
+    _dev(v_scale, "v_scale", (torch.float16, torch.int16), (num_pages, Hkv, P))
+    return num_pages, Hkv, P, D
+
+
+def _lens(block_table, context_lens, draft_lens, B):
+    torch = _torch()
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages_per_seq]")
+    _dev(block_table, "block_table", (torch.int32,))
+    _dev(context_lens, "context_lens", (torch.int32,), (B,))
+    _dev(draft_lens, "draft_lens", (torch.int32,), (B,))
+    return block_table.shape[1]
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def splash_kv_append_int8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_table,
+                          context_lens, draft_lens, stream=None):
+    """Quantise k_new/v_new [B][T_max][Hkv][D] (fp32 or bf16) into the int8 pools."""
+    torch = _torch()
+    if k_new.dim() != 4:
+        raise ValueError("k_new must be [B][T_max][Hkv][D]")
+    B, T_max, Hkv_src, D_src = k_new.shape
+    _dev(k_new, "k_new", (torch.float32, torch.bfloat16))
+    _dev(v_new, "v_new", (k_new.dtype,), tuple(k_new.shape))
+    num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
+    if (Hkv_src, D_src) != (Hkv, D):
+        raise ValueError("k_new heads / head dim do not match the pools")
+    maxp = _lens(block_table, context_lens, draft_lens, B)
+    src = SPLASH_SRC_F32 if k_new.dtype == torch.float32 else SPLASH_SRC_BF16
+    rc = _lib().splash_kv_append_int8(
+        k_new.data_ptr(), v_new.data_ptr(), src, k_pool.data_ptr(), v_pool.data_ptr(),
+        k_scale.data_ptr(), v_scale.data_ptr(), block_table.data_ptr(), maxp,
+        context_lens.data_ptr(), draft_lens.data_ptr(), B, T_max, Hkv, D, P, num_pages,
+        _stream(stream))
+    _check(rc, "splash_kv_append_int8")
+
+
+def splash_verify_attn_default_splits(B, Hkv, max_context_len, P=PAGE_SIZE, D=256):
+    rc = _lib().splash_verify_attn_default_splits(int(B), int(Hkv), int(max_context_len), int(P), int(D))
+    if rc < 0:
+        _check(-rc, "splash_verify_attn_default_splits")
+    return rc
+
+
+def splash_verify_attn_split_pages(max_context_len, P, num_splits):
+    rc = _lib().splash_verify_attn_split_pages(int(max_context_len), int(P), int(num_splits))
+    if rc < 0:
+        _check(-rc, "splash_verify_attn_split_pages")
+    return rc
+
+
+def splash_verify_attn_workspace_bytes(B, T_max, Hq, D, num_splits):
+    return int(_lib().splash_verify_attn_workspace_bytes(int(B), int(T_max), int(Hq), int(D),
+                                                         int(num_splits)))
+
+
+def effective_splits(max_context_len, P, num_splits):
+    """Number of splits that hold at least one page for a requested split count."""
+    if max_context_len <= 0:
+        return 1
+    L = splash_verify_attn_split_pages(max_context_len, P, num_splits)
+    n_pages = -(-max_context_len // P)
+    return -(-n_pages // L)
+
+
+def splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                       draft_lens, max_context_len, sm_scale, num_splits=0, workspace=None,
+                       stream=None):
+    """Block-verify attention; writes out[b][t][h][:] for t < draft_lens[b].
+
+    workspace: a byte tensor of at least splash_verify_attn_workspace_bytes(...)
+    for the splits that run, or None to let this binding allocate one with torch.
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B][T_max][Hq][D]")
+    B, T_max, Hq, Dq = q.shape
+    _dev(q, "q", (torch.bfloat16, torch.int16))
+    _dev(out, "out", (torch.bfloat16, torch.int16), tuple(q.shape))
+    num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
+    if Dq != D:
+        raise ValueError("q head dim does not match the pools")
+    maxp = _lens(block_table, context_lens, draft_lens, B)
+    S_req = num_splits if num_splits > 0 else (
+        splash_verify_attn_default_splits(B, Hkv, max_context_len, P, D) if B and max_context_len else 1)
+    S = effective_splits(max_context_len, P, S_req)
+    need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _dev(workspace, "workspace", (torch.uint8, torch.int8, torch.float32))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = _lib().splash_verify_attn(
+        q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),
+        draft_lens.data_ptr(), B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len),
+        float(sm_scale), int(S_req), ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "splash_verify_attn")
+    return out
+
+
+def splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                                 draft_lens, max_context_len, sm_scale, num_splits, part_o,
+                                 part_lse, stream=None):
+    """Partial rows per context split: part_o [B][Hq][T_max][S][D], part_lse [B][Hq][T_max][S]."""
+    torch = _torch()
+    B, T_max, Hq, Dq = q.shape
+    _dev(q, "q", (torch.bfloat16, torch.int16))
+    num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
+    maxp = _lens(block_table, context_lens, draft_lens, B)
+    S = int(num_splits)
+    _dev(part_o, "part_o", (torch.float32,), (B, Hq, T_max, S, D))
+    _dev(part_lse, "part_lse", (torch.float32,), (B, Hq, T_max, S))
+    rc = _lib().splash_verify_attn_partition(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+        block_table.data_ptr(), maxp, context_lens.data_ptr(), draft_lens.data_ptr(), B, T_max,
+        Hq, Hkv, D, P, num_pages, int(max_context_len), float(sm_scale), S, part_o.data_ptr(),
+        part_lse.data_ptr(), _stream(stream))
+    _check(rc, "splash_verify_attn_partition")
+
+
+def splash_verify_attn_splitk_merge(part_o, part_lse, out, draft_lens, stream=None):
+    """Merge S splits: part_o [B][Hq][T_max][S][D] fp32 -> out [B][T_max][Hq][D] bf16."""
+    torch = _torch()
+    B, Hq, T_max, S, D = part_o.shape
+    _dev(part_o, "part_o", (torch.float32,))
+    _dev(part_lse, "part_lse", (torch.float32,), (B, Hq, T_max, S))
+    _dev(out, "out", (torch.bfloat16, torch.int16), (B, T_max, Hq, D))
+    _dev(draft_lens, "draft_lens", (torch.int32,), (B,))
+    rc = _lib().splash_verify_attn_splitk_merge(part_o.data_ptr(), part_lse.data_ptr(),
+                                                out.data_ptr(), draft_lens.data_ptr(), B, T_max,
+                                                Hq, D, S, _stream(stream))
+    _check(rc, "splash_verify_attn_splitk_merge")
+    return out

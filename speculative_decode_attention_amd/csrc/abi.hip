@@ -1,0 +1,204 @@
+// abi.hip -- the C ABI (include/splash_attn.h): argument checks, the split-K
+// preset, workspace sizing and kernel launches.  No call allocates, keeps
+// per-call state or synchronises the host; the only state is a per-device
+// cache of the compute-unit count used by the preset.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/splash_attn.h"
+#include "launch.h"
+
+using namespace splash;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxVerifyT = 16;
+// smallest number of pages a split is given by the preset: below this the
+// fixed cost of a workgroup (loading Q, writing partials) dominates its work
+constexpr int kMinPagesPerSplit = 8;
+
+std::mutex g_cu_mutex;
+int g_cu_count[kMaxDevices] = {0};
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (g_cu_count[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return -1;
+        g_cu_count[dev] = cus;
+    }
+    return g_cu_count[dev];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int pages_per_split(int max_context_len, int P, int num_splits) {
+    const int n_pages = ceil_div(max_context_len, P);
+    int L = ceil_div(n_pages, num_splits);
+    L = ceil_div(L, kPagesPerIter) * kPagesPerIter;
+    return L < kPagesPerIter ? kPagesPerIter : L;
+}
+
+int check_verify_common(const void* q, const void* k_pool, const void* v_pool, const void* k_scale,
+                        const void* v_scale, const void* block_table, const void* context_lens,
+                        const void* draft_lens, int max_pages_per_seq, int B, int T_max, int Hq,
+                        int Hkv, int D, int P, int num_pages, int max_context_len, float sm_scale) {
+    if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !block_table || !context_lens || !draft_lens)
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T_max < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || num_pages <= 0 ||
+        max_context_len < 0 || max_pages_per_seq < 0)
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv != 0 || !std::isfinite(sm_scale)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if ((long)ceil_div(max_context_len, P) > (long)max_pages_per_seq) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (P != kPage || T_max > kMaxVerifyT || !verify_supported(D, Hq / Hkv)) return SPLASH_ERR_UNSUPPORTED;
+    return SPLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* splash_status_string(int status) {
+    switch (status) {
+        case SPLASH_OK: return "ok";
+        case SPLASH_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case SPLASH_ERR_UNSUPPORTED: return "shape outside the compiled set";
+        case SPLASH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SPLASH_ERR_LAUNCH: return "kernel launch failed";
+        case SPLASH_ERR_DEVICE: return "device query failed";
+        default: return "unknown status";
+    }
+}
+
+int splash_kv_append_int8(const void* k_new, const void* v_new, int src_dtype, int8_t* k_pool,
+                          int8_t* v_pool, uint16_t* k_scale, uint16_t* v_scale,
+                          const int32_t* block_table, int max_pages_per_seq,
+                          const int32_t* context_lens, const int32_t* draft_lens, int B, int T_max,
+                          int Hkv, int D, int P, int num_pages, void* stream) {
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_table ||
+        !context_lens || !draft_lens)
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T_max < 0 || Hkv <= 0 || D <= 0 || P <= 0 || num_pages <= 0 || max_pages_per_seq <= 0)
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (src_dtype != SPLASH_SRC_F32 && src_dtype != SPLASH_SRC_BF16) return SPLASH_ERR_INVALID_ARGUMENT;
+    const size_t elem = src_dtype == SPLASH_SRC_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % (elem * (D / 64 > 0 ? D / 64 : 1)))
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (P != kPage || !append_supported(D)) return SPLASH_ERR_UNSUPPORTED;
+    if (B == 0 || T_max == 0) return SPLASH_OK;
+    AppendArgs a{k_new, v_new, src_dtype == SPLASH_SRC_BF16, k_pool, v_pool, k_scale, v_scale,
+                 block_table, max_pages_per_seq, context_lens, draft_lens, B, T_max, Hkv, D};
+    return launch_kv_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
+                                                                              : SPLASH_ERR_LAUNCH;
+}
+
+int splash_verify_attn_split_pages(int max_context_len, int P, int num_splits) {
+    if (max_context_len < 0 || P <= 0 || num_splits <= 0) return -SPLASH_ERR_INVALID_ARGUMENT;
+    return pages_per_split(max_context_len, P, num_splits);
+}
+
+int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P, int D) {
+    if (B <= 0 || Hkv <= 0 || max_context_len < 0 || P <= 0 || D <= 0) return -SPLASH_ERR_INVALID_ARGUMENT;
+    const int cus = device_cu_count();
+    if (cus <= 0) return -SPLASH_ERR_DEVICE;
+    const long items = (long)B * Hkv;
+    int S = ceil_div(cus, items);                         // one workgroup per compute unit
+    const int n_pages = ceil_div(max_context_len, P);
+    const int cap = ceil_div(n_pages, kMinPagesPerSplit);
+    if (S > cap) S = cap;
+    return S < 1 ? 1 : S;
+}
+
+size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits) {
+    if (B <= 0 || T_max <= 0 || Hq <= 0 || D <= 0 || num_splits <= 1) return 0;
+    const size_t rows = (size_t)B * Hq * T_max * num_splits;
+    return align_up(rows * D * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+}
+
+int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                       const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
+                       int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                       int max_context_len, float sm_scale, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                                 draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
+                                 max_context_len, sm_scale);
+    if (rc != SPLASH_OK) return rc;
+    if (!out || !aligned16(out) || num_splits < 0) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;   // no draft row can exist
+    if (num_splits == 0) {
+        num_splits = splash_verify_attn_default_splits(B, Hkv, max_context_len, P, D);
+        if (num_splits < 0) return -num_splits;
+    }
+    const int L = pages_per_split(max_context_len, P, num_splits);
+    const int S = ceil_div(ceil_div(max_context_len, P), L);     // splits that hold pages
+    VerifyArgs a{q, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, block_table,
+                 max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale, S, L};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (S == 1) {
+        a.out = out;
+        return launch_verify_partition(a, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
+    }
+    const size_t need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S);
+    if (!workspace || !aligned16(workspace)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return SPLASH_ERR_WORKSPACE_TOO_SMALL;
+    const size_t rows = (size_t)B * Hq * T_max * S;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align_up(rows * D * sizeof(float), 256));
+    if (launch_verify_partition(a, st) != hipSuccess) return SPLASH_ERR_LAUNCH;
+    MergeArgs m{a.part_o, a.part_lse, out, draft_lens, B, T_max, Hq, D, S};
+    return launch_splitk_merge(m, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
+}
+
+int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,
+                                 const uint16_t* k_scale, const uint16_t* v_scale,
+                                 const int32_t* block_table, int max_pages_per_seq,
+                                 const int32_t* context_lens, const int32_t* draft_lens, int B,
+                                 int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                                 int max_context_len, float sm_scale, int num_splits, float* part_o,
+                                 float* part_lse, void* stream) {
+    int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                                 draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
+                                 max_context_len, sm_scale);
+    if (rc != SPLASH_OK) return rc;
+    if (!part_o || !part_lse || !aligned16(part_o) || !aligned16(part_lse) || num_splits <= 0)
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;
+    const int L = pages_per_split(max_context_len, P, num_splits);
+    VerifyArgs a{q, nullptr, part_o, part_lse, k_pool, v_pool, k_scale, v_scale, block_table,
+                 max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale,
+                 num_splits, L};
+    return launch_verify_partition(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
+                                                                                     : SPLASH_ERR_LAUNCH;
+}
+
+int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse, uint16_t* out,
+                                    const int32_t* draft_lens, int B, int T_max, int Hq, int D,
+                                    int num_splits, void* stream) {
+    if (!part_o || !part_lse || !out || !draft_lens) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T_max < 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (!aligned16(part_o) || !aligned16(out)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (D != 64 && D != 128 && D != 256) return SPLASH_ERR_UNSUPPORTED;
+    if (B == 0 || T_max == 0) return SPLASH_OK;
+    MergeArgs m{part_o, part_lse, out, draft_lens, B, T_max, Hq, D, num_splits};
+    return launch_splitk_merge(m, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
+                                                                                 : SPLASH_ERR_LAUNCH;
+}
+
+}  // extern "C"

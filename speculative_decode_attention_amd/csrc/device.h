@@ -1,0 +1,57 @@
+// device.h -- types and small helpers shared by the gfx950 kernels of the
+// verify-attention library.  Internal header; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splash {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bit_cast(const From& f) {
+    static_assert(sizeof(To) == sizeof(From), "bit_cast size");
+    return __builtin_bit_cast(To, f);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = bit_cast<uint32_t>(f);
+    if ((u & 0x7f800000u) == 0x7f800000u)            // inf / nan: truncate, keep nan quiet
+        return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Wave-wide reductions over all 64 lanes (result in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 lane-swap instructions: swapping a register with itself leaves, in the
+// two results, each lane's own value and its partner's (16 or 32 lanes away).
+__device__ __forceinline__ float group4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
+    v = fmaxf(bit_cast<float>(a[0]), bit_cast<float>(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
+    return fmaxf(bit_cast<float>(b[0]), bit_cast<float>(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
+    v = bit_cast<float>(a[0]) + bit_cast<float>(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
+    return bit_cast<float>(b[0]) + bit_cast<float>(b[1]);
+}
+
+}  // namespace splash

@@ -1,0 +1,62 @@
+// launch.h -- argument bundles and launchers between the C ABI (abi.hip) and
+// the kernels.  Internal header; the C ABI is include/splash_attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace splash {
+
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    bool src_bf16;
+    int8_t* k_pool;
+    int8_t* v_pool;
+    uint16_t* k_scale;
+    uint16_t* v_scale;
+    const int32_t* block_table;
+    int max_pages_per_seq;
+    const int32_t* context_lens;
+    const int32_t* draft_lens;
+    int B, T_max, Hkv, D;
+};
+
+struct VerifyArgs {
+    const uint16_t* q;
+    uint16_t* out;             // final bf16 rows (one split)            or nullptr
+    float* part_o;             // fp32 partial rows (several splits)      or nullptr
+    float* part_lse;           // natural-log log-sum-exps per split      or nullptr
+    const int8_t* k_pool;
+    const int8_t* v_pool;
+    const uint16_t* k_scale;
+    const uint16_t* v_scale;
+    const int32_t* block_table;
+    int max_pages_per_seq;
+    const int32_t* context_lens;
+    const int32_t* draft_lens;
+    int B, T_max, Hq, Hkv, D;
+    float sm_scale;
+    int num_splits;            // grid size along the context (S used in the layouts)
+    int pages_per_split;       // L, a multiple of kPagesPerIter
+};
+
+struct MergeArgs {
+    const float* part_o;
+    const float* part_lse;
+    uint16_t* out;
+    const int32_t* draft_lens;
+    int B, T_max, Hq, D, num_splits;
+};
+
+constexpr int kPage = 16;            // tokens per page (the compiled page size)
+constexpr int kPagesPerIter = 4;    // pages a workgroup of the partition kernel takes per step
+
+bool append_supported(int D);
+bool verify_supported(int D, int G);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_splitk_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace splash

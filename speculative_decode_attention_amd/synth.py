@@ -61,7 +61,7 @@ class Workload:
     draft_lens: np.ndarray       # int32 [B]
     # initial pool contents: poison everywhere except directly placed tokens
     k_pool: np.ndarray           # int8 [num_pages][Hkv][P][D]
-    v_pool: np.ndarray           # int8 [num_pages][Hkv][D][P]
+    v_pool: np.ndarray           # int8 [num_pages][Hkv][P/8][D][8]
     k_scale: np.ndarray          # fp16 bits uint16 [num_pages][Hkv][P]
     v_scale: np.ndarray          # fp16 bits uint16 [num_pages][Hkv][P]
     appends: list = field(default_factory=list)   # AppendPhase, applied in order
@@ -85,7 +85,7 @@ class Workload:
 
 def empty_pools(num_pages: int, Hkv: int, P: int, D: int):
     k_pool = np.full((num_pages, Hkv, P, D), POISON_CODE, dtype=np.int8)
-    v_pool = np.full((num_pages, Hkv, D, P), POISON_CODE, dtype=np.int8)
+    v_pool = np.full((num_pages, Hkv, P // 8, D, 8), POISON_CODE, dtype=np.int8)
     k_scale = np.full((num_pages, Hkv, P), POISON_SCALE_F16, dtype=np.uint16)
     v_scale = np.full((num_pages, Hkv, P), POISON_SCALE_F16, dtype=np.uint16)
     return k_pool, v_pool, k_scale, v_scale
@@ -95,7 +95,8 @@ def place_tokens(k_pool, v_pool, k_scale, v_scale, bt_row, first_pos, k, v, ks, 
     """Store token rows first_pos.. at the (page, slot) the block-table row names.
 
     k, v: int8 [n][Hkv][D]; ks, vs: fp16 bits [n][Hkv].  K pages are
-    [Hkv][P][D], V pages [Hkv][D][P].
+    [Hkv][P][D] (token rows); V pages are [Hkv][P/8][D][8] (two d-major tiles of
+    8 tokens each).
     """
     P = k_pool.shape[2]
     pos = first_pos + np.arange(k.shape[0])
@@ -103,7 +104,7 @@ def place_tokens(k_pool, v_pool, k_scale, v_scale, bt_row, first_pos, k, v, ks, 
     slots = pos % P
     for g in range(k_pool.shape[1]):
         k_pool[pages, g, slots, :] = k[:, g, :]
-        v_pool[pages, g, :, slots] = v[:, g, :]
+        v_pool[pages, g, slots // 8, :, slots % 8] = v[:, g, :]
         k_scale[pages, g, slots] = ks[:, g]
         v_scale[pages, g, slots] = vs[:, g]
 

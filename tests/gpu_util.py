@@ -1,0 +1,141 @@
+"""Helpers shared by the GPU tests: uploads, bf16 decoding, the attention
+tolerance, and workloads prepared once per session (oracle pools and GPU pools
+built from the same seeded source rows)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import speculative_decode_attention_amd as sda
+from speculative_decode_attention_amd import synth
+
+BF16_NAN = 0x7FC0
+
+# tolerance: relative L2 <= 2e-3 over the valid rows, and every element within
+# 1e-2 plus half a bf16 ulp of the reference (rounding even the exact fp64
+# answer to bf16 moves an element by up to half an ulp, which exceeds 1e-2 when
+# |o| >= 2.56)
+REL_L2 = 2e-3
+ABS = 1e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def up(a):
+    torch = torch_mod()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def bf16_to_f64(bits):
+    bits = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return bits.view(np.float32).astype(np.float64)
+
+
+def half_ulp_bf16(ref):
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 8), 0.0)
+
+
+def attn_error(got, ref):
+    """got, ref: fp64 arrays of the same shape (valid rows only)."""
+    diff = got - ref
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    bound = ABS + half_ulp_bf16(ref)
+    excess = float(np.max(np.abs(diff) - bound)) if diff.size else -1.0
+    ref_bf16 = bf16_to_f64(_round_bf16(ref))
+    ulps = float(np.max(np.abs(got - ref_bf16) / np.maximum(2 * half_ulp_bf16(ref), 1e-300))) if diff.size else 0.0
+    return dict(rel_l2=rel, max_abs=float(np.max(np.abs(diff))) if diff.size else 0.0,
+                bound_excess=excess, max_ulps_vs_bf16_ref=ulps,
+                finite=bool(np.all(np.isfinite(got))))
+
+
+def _round_bf16(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+
+
+def assert_attn_ok(got, ref, where):
+    e = attn_error(got, ref)
+    log(f"  {where}: rel_l2={e['rel_l2']:.3e} max|err|={e['max_abs']:.3e} "
+        f"bound_excess={e['bound_excess']:.2e} ulps_vs_bf16(ref)={e['max_ulps_vs_bf16_ref']:.2f}")
+    assert e["finite"], f"{where}: non-finite output"
+    assert e["rel_l2"] <= REL_L2, f"{where}: relative L2 {e['rel_l2']:.3e}"
+    assert e["bound_excess"] <= 0, f"{where}: an element exceeds 1e-2 + half a bf16 ulp"
+    return e
+
+
+class Prepared:
+    """One workload with oracle pools (host) and GPU pools built by the GPU append."""
+
+    def __init__(self, wl: synth.Workload):
+        self.wl = wl
+        orc = oracle.load()
+        self.pools = [a.copy() for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+        for ph in wl.appends:
+            orc.kv_append_int8(ph.k_src, ph.v_src, *self.pools, ph.block_table, ph.context_lens,
+                               ph.draft_lens)
+        self.g_pools = [up(a) for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+        for ph in wl.appends:
+            sda.splash_kv_append_int8(up(ph.k_src), up(ph.v_src), *self.g_pools, up(ph.block_table),
+                                      up(ph.context_lens), up(ph.draft_lens))
+        torch_mod().cuda.synchronize()
+        self.q = up(wl.q)
+        self.bt = up(wl.block_table)
+        self.ctx = up(wl.context_lens)
+        self.dl = up(wl.draft_lens)
+
+    def pools_equal(self):
+        names = ("k_pool", "v_pool", "k_scale", "v_scale")
+        for name, host, dev in zip(names, self.pools, self.g_pools):
+            got = dev.cpu().numpy()
+            if host.dtype == np.uint16:
+                got = got.view(np.uint16)
+            if not np.array_equal(got, host):
+                bad = np.flatnonzero(got.ravel() != host.ravel())
+                return f"{name}: {bad.size} bytes differ, first at flat index {bad[0]}"
+        return None
+
+    def run(self, num_splits=0, out=None):
+        torch = torch_mod()
+        wl = self.wl
+        if out is None:
+            out = torch.full(tuple(wl.q.shape), BF16_NAN, dtype=torch.int16, device="cuda")
+        sda.splash_verify_attn(self.q, out, *self.g_pools, self.bt, self.ctx, self.dl,
+                               wl.max_context_len, wl.sm_scale, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out
+
+    def valid_rows(self):
+        wl = self.wl
+        return np.array([(b, t, h) for b in range(wl.B) for t in range(int(wl.draft_lens[b]))
+                         for h in range(wl.Hq)], dtype=np.int32)
+
+    def oracle_rows(self, rows):
+        wl = self.wl
+        return oracle.load().verify_attn_rows(wl.q, *self.pools, wl.block_table, wl.context_lens,
+                                              wl.draft_lens, wl.Hkv, wl.sm_scale, rows)
+
+
+_cache = {}
+
+
+def prepared_config(cfg: int) -> Prepared:
+    if cfg not in _cache:
+        log(f"[prepare] config {cfg}: {synth.CONFIG_NAMES[cfg]}")
+        _cache.clear()                      # one large workload resident at a time
+        _cache[cfg] = Prepared(synth.make_config(cfg))
+    return _cache[cfg]

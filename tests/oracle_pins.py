@@ -229,7 +229,8 @@ def pin_bf16_source_equals_fp32(orc, seed=15):
 # --------------------------------------------------------------------------
 def pin_append_placement(orc, seed=16):
     """Rows k * 2^-5 (codes known without any quantiser) land at ctx - d + t:
-    K at [page][g][slot][:], V transposed at [page][g][:][slot]; nothing else changes."""
+    K at [page][g][slot][:], V in tile slot // 8 at [page][g][slot // 8][:][slot % 8];
+    nothing else changes."""
     rng = np.random.default_rng(seed)
     B, T_max, Hkv, D, P, num_pages = 3, 21, 2, 64, 16, 40
     ctx = np.array([45, 21, 70], np.int32)
@@ -256,10 +257,10 @@ def pin_append_placement(orc, seed=16):
             page, slot = bt[b, pos // P], pos % P
             for g in range(Hkv):
                 assert np.array_equal(kp[page, g, slot, :].astype(np.int64), kcodes[b, t, g])
-                assert np.array_equal(vp[page, g, :, slot].astype(np.int64), vcodes[b, t, g])
+                assert np.array_equal(vp[page, g, slot // 8, :, slot % 8].astype(np.int64), vcodes[b, t, g])
                 assert ks[page, g, slot] == s_bits and vs[page, g, slot] == s_bits
                 touched_k[page, g, slot, :] = True
-                touched_v[page, g, :, slot] = True
+                touched_v[page, g, slot // 8, :, slot % 8] = True
                 touched_s[page, g, slot] = True
     assert np.array_equal(kp[~touched_k], kp0[~touched_k])
     assert np.array_equal(vp[~touched_v], vp0[~touched_v])
@@ -297,7 +298,7 @@ def pin_attn_dense_exact_values(orc, seed=21):
     rng = np.random.default_rng(seed)
     for (Hq, Hkv, D, P, ctx, dl, T_max) in [(6, 2, 16, 16, [37, 50], [3, 5], 5),
                                            (8, 2, 64, 16, [256], [4], 4),
-                                           (4, 4, 32, 4, [9, 1, 16], [2, 1, 16], 16)]:
+                                           (4, 4, 32, 8, [9, 1, 16], [2, 1, 16], 16)]:
         wl = synth.make_workload("exact", int(rng.integers(1 << 30)), B=len(ctx), context_lens=ctx,
                                  T_max=T_max, draft_lens=dl, Hq=Hq, Hkv=Hkv, D=D, P=P,
                                  num_pages=64, values="direct", sm_scale=1.0 / np.sqrt(D))
@@ -455,10 +456,12 @@ def pin_split_equals_unsplit(orc, seed=29):
     wl = _small_direct(seed, context_lens=[37, 80], draft_lens=[3, 5], num_pages=24)
     full = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
                            wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    n_pages = -(-wl.max_context_len // wl.P)
     for S in (1, 2, 3, 5, 9):
+        L = -(-n_pages // S)
         po, pl = orc.verify_attn_split(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale,
                                        wl.block_table, wl.context_lens, wl.draft_lens, wl.Hkv,
-                                       wl.sm_scale, S, wl.max_context_len)
+                                       wl.sm_scale, S, L)
         merged = lse_merge_fp64(po, pl)                 # [B][Hq][T][D]
         for b in range(wl.B):
             d = int(wl.draft_lens[b])
@@ -469,7 +472,7 @@ def pin_split_equals_unsplit(orc, seed=29):
     # the merge entry point (fp32 partials in, fp64 out) on the split path's output
     po, pl = orc.verify_attn_split(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale,
                                    wl.block_table, wl.context_lens, wl.draft_lens, wl.Hkv,
-                                   wl.sm_scale, 4, wl.max_context_len)
+                                   wl.sm_scale, 4, 2)
     po32 = np.nan_to_num(po).astype(np.float32)
     pl32 = np.where(np.isnan(pl), -np.inf, pl).astype(np.float32)
     out = orc.splitk_merge(po32, pl32, wl.draft_lens, wl.T_max)

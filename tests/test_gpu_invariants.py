@@ -1,0 +1,170 @@
+"""GPU invariants and edge cases of block-verify attention (through the C ABI).
+
+Bit-level properties hold because the kernel's reduction order depends only on
+token positions: repeat runs, a permutation of physical page ids, and shared
+prefix pages against private copies all give identical bits.  Edge cases:
+contexts shorter than a page or not a multiple of it, drafts that fill the
+whole context, requests with no draft, NaN in unused query rows, bf16 append
+sources, the (D=64, G=4) and (D=128, G=8) shapes, fewer than 16 drafts.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import oracle  # noqa: E402
+import speculative_decode_attention_amd as sda  # noqa: E402
+from speculative_decode_attention_amd import synth  # noqa: E402
+from gpu_util import BF16_NAN, Prepared, assert_attn_ok, bf16_to_f64, log, up  # noqa: E402
+
+
+def small(seed, **kw):
+    base = dict(B=3, context_lens=[333, 64, 1000], T_max=16, draft_lens=[16, 7, 11], Hq=24, Hkv=4,
+                D=256, num_pages=160)
+    base.update(kw)
+    return Prepared(synth.make_workload("inv", seed, **base))
+
+
+def check_full(prep, out, where):
+    wl = prep.wl
+    rows = prep.valid_rows()
+    if len(rows) == 0:
+        return
+    got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
+    assert_attn_ok(got, prep.oracle_rows(rows), where)
+    for b in range(wl.B):
+        assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN), f"{where}: row written"
+
+
+@pytest.mark.parametrize("S", [1, 5])
+def test_repeat_runs_bit_identical(S):
+    prep = small(1)
+    a = prep.run(num_splits=S).cpu().numpy()
+    b = prep.run(num_splits=S).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def test_page_permutation_bit_identical():
+    prep = small(2)
+    base = prep.run(num_splits=3).cpu().numpy()
+    wl = prep.wl
+    perm = np.random.default_rng(9).permutation(wl.num_pages).astype(np.int32)
+    moved = [np.empty_like(a) for a in prep.pools]
+    for dst, src in zip(moved, prep.pools):
+        dst[perm] = src
+    g = [up(a) for a in moved]
+    out = torch.full(tuple(wl.q.shape), BF16_NAN, dtype=torch.int16, device="cuda")
+    sda.splash_verify_attn(prep.q, out, *g, up(perm[wl.block_table]), prep.ctx, prep.dl,
+                           wl.max_context_len, wl.sm_scale, num_splits=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), base)
+
+
+def test_shared_prefix_pages_equal_private_copies():
+    prep = small(3, B=4, context_lens=[26624 // 16 * 1 + 400, 700, 656, 1200], draft_lens=[16, 16, 3, 9],
+                 shared_prefix=512, num_pages=400)
+    wl = prep.wl
+    shared = prep.run(num_splits=4).cpu().numpy()
+    check_full(prep, shared, "shared prefix")
+    pools = [a.copy() for a in prep.pools]
+    bt = wl.block_table.copy()
+    used = set(wl.pages_used.tolist())
+    free = [p for p in range(wl.num_pages) if p not in used]
+    n_prefix = 512 // 16
+    for b in range(1, wl.B):
+        for i in range(n_prefix):
+            dst = free.pop()
+            for arr in pools:
+                arr[dst] = arr[bt[b, i]]
+            bt[b, i] = dst
+    g = [up(a) for a in pools]
+    out = torch.full(tuple(wl.q.shape), BF16_NAN, dtype=torch.int16, device="cuda")
+    sda.splash_verify_attn(prep.q, out, *g, up(bt), prep.ctx, prep.dl, wl.max_context_len,
+                           wl.sm_scale, num_splits=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), shared)
+
+
+@pytest.mark.parametrize("case", [
+    dict(context_lens=[1, 5, 16], draft_lens=[1, 5, 16]),             # drafts fill the context
+    dict(context_lens=[17, 31, 33], draft_lens=[16, 2, 1]),           # ragged page tails
+    dict(context_lens=[100, 50, 400], draft_lens=[0, 16, 0]),         # requests with no draft
+    dict(context_lens=[4096, 15, 2000], draft_lens=[1, 1, 1], T_max=1),   # T = 1: plain decode
+    dict(context_lens=[300, 301, 302], draft_lens=[4, 8, 12], T_max=12),
+])
+@pytest.mark.parametrize("S", [0, 1, 9])
+def test_edge_shapes(case, S):
+    prep = small(4, **case, num_pages=400)
+    out = prep.run(num_splits=S).cpu().numpy()
+    check_full(prep, out, f"{case} S={S}")
+
+
+def test_nan_query_rows_do_not_leak():
+    prep = small(5, draft_lens=[3, 16, 1], nan_pad_q=True)
+    out = prep.run(num_splits=4).cpu().numpy()
+    check_full(prep, out, "NaN-padded q")
+
+
+@pytest.mark.parametrize("shape", [(8, 2, 64, 4), (16, 2, 128, 16), (24, 4, 256, 5)])
+def test_other_compiled_shapes(shape):
+    Hq, Hkv, D, T = shape
+    prep = small(6, B=2, context_lens=[700, 90], draft_lens=[T, max(1, T // 2)], T_max=T, Hq=Hq,
+                 Hkv=Hkv, D=D)
+    assert prep.pools_equal() is None
+    for S in (1, 3):
+        out = prep.run(num_splits=S).cpu().numpy()
+        check_full(prep, out, f"shape {shape} S={S}")
+
+
+def test_direct_value_pools_tiny_config_all_splits():
+    prep = Prepared(synth.make_config(1))
+    for S in (1, 2, 3, 4):
+        out = prep.run(num_splits=S).cpu().numpy()
+        check_full(prep, out, f"config 1 S={S}")
+
+
+def test_append_from_bf16_source_bit_exact():
+    wl = synth.make_workload("bf16", 7, B=2, context_lens=[90, 40], T_max=16, draft_lens=[16, 5],
+                             Hq=24, Hkv=4, D=256, num_pages=16)
+    orc = oracle.load()
+    ph = wl.appends[-1]
+    kb = (ph.k_src.view(np.uint32) >> 16).astype(np.uint16)
+    vb = (ph.v_src.view(np.uint32) >> 16).astype(np.uint16)
+    host = [a.copy() for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+    orc.kv_append_int8(kb, vb, *host, ph.block_table, ph.context_lens, ph.draft_lens)
+    dev = [up(a) for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+    sda.splash_kv_append_int8(up(kb).view(torch.bfloat16), up(vb).view(torch.bfloat16), *dev,
+                              up(ph.block_table), up(ph.context_lens), up(ph.draft_lens))
+    torch.cuda.synchronize()
+    for h, d in zip(host, dev):
+        got = d.cpu().numpy()
+        assert np.array_equal(got.view(h.dtype) if h.dtype == np.uint16 else got, h)
+
+
+def test_append_quantiser_edge_rows_bit_exact():
+    """Zero rows, subnormal and tiny scales, exact ties, large magnitudes."""
+    rng = np.random.default_rng(8)
+    B, T, Hkv, D = 1, 16, 4, 256
+    x = rng.standard_normal((B, T, Hkv, D)).astype(np.float32)
+    x[0, 0] = 0.0
+    x[0, 1] *= np.float32(1e-9)                      # scale underflows to 0
+    x[0, 2] *= np.float32(3e-5)                      # subnormal binary16 scale
+    x[0, 3] = (rng.integers(-127, 128, (Hkv, D)) * 2.0 ** -5).astype(np.float32)
+    x[0, 3, :, 0] = 127 * 2.0 ** -5
+    x[0, 4] = ((rng.integers(-120, 120, (Hkv, D)) + 0.5) * 2.0 ** -5).astype(np.float32)
+    x[0, 4, :, 0] = 127 * 2.0 ** -5                  # exact ties
+    x[0, 5] *= np.float32(3000.0)
+    bt = np.arange(4, dtype=np.int32)[None]
+    ctx = np.array([40], np.int32)
+    dl = np.array([16], np.int32)
+    k_pool, v_pool, ks, vs = synth.empty_pools(8, Hkv, 16, D)
+    host = [a.copy() for a in (k_pool, v_pool, ks, vs)]
+    oracle.load().kv_append_int8(x, x[:, ::-1].copy(), *host, bt, ctx, dl)
+    dev = [up(a) for a in (k_pool, v_pool, ks, vs)]
+    sda.splash_kv_append_int8(up(x), up(x[:, ::-1].copy()), *dev, up(bt), up(ctx), up(dl))
+    torch.cuda.synchronize()
+    for h, d in zip(host, dev):
+        got = d.cpu().numpy()
+        assert np.array_equal(got.view(h.dtype) if h.dtype == np.uint16 else got, h)

@@ -29,8 +29,10 @@ MUTANTS = {
     "bf16_widen_shift": ("return bits_f32((uint32_t)b << 16);", "return bits_f32((uint32_t)b << 15);"),
     # append placement
     "append_pos_off_by_one": ("int pos = n - dl + t;", "int pos = n - dl + t + 1;"),
-    "v_layout_like_k": ("{ return (((size_t)page * Hkv + g) * D + d) * P + slot; }",
+    "v_layout_like_k": ("{ return ((((size_t)page * Hkv + g) * (P / 8) + slot / 8) * D + d) * 8 + slot % 8; }",
                         "{ return (((size_t)page * Hkv + g) * P + slot) * D + d; }"),
+    "v_tile_dropped": ("{ return ((((size_t)page * Hkv + g) * (P / 8) + slot / 8) * D + d) * 8 + slot % 8; }",
+                       "{ return ((((size_t)page * Hkv + g) * (P / 8)) * D + d) * 8 + slot % 8; }"),
     "append_v_scale_into_k": ("k_scale[s_index(page, g, slot, Hkv, P)] = s16;",
                               "v_scale[s_index(page, g, slot, Hkv, P)] = s16;"),
     # attention
