@@ -39,19 +39,34 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
-// gfx950 lane-swap instructions: swapping a register with itself leaves, in the
-// two results, each lane's own value and its partner's (16 or 32 lanes away).
+// gfx950 lane-swap instructions.  Swapping a register with itself exchanges the
+// odd 16-lane rows of one copy with the even rows of the other, so the two
+// results hold, in every lane, its own value and its partner's (16 or 32 lanes
+// away).  The results are copied to scalars before use: a bit cast applied to a
+// vector element in place can read element 0.
+__device__ __forceinline__ void lane_swap16(float v, float& own, float& partner) {
+    const u32x2_t a = __builtin_amdgcn_permlane16_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
+    const uint32_t x = a[0], y = a[1];
+    own = bit_cast<float>(x);
+    partner = bit_cast<float>(y);
+}
+__device__ __forceinline__ void lane_swap32(float v, float& own, float& partner) {
+    const u32x2_t a = __builtin_amdgcn_permlane32_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
+    const uint32_t x = a[0], y = a[1];
+    own = bit_cast<float>(x);
+    partner = bit_cast<float>(y);
+}
 __device__ __forceinline__ float group4_max(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
-    v = fmaxf(bit_cast<float>(a[0]), bit_cast<float>(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
-    return fmaxf(bit_cast<float>(b[0]), bit_cast<float>(b[1]));
+    float a, b;
+    lane_swap16(v, a, b);
+    lane_swap32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
 __device__ __forceinline__ float group4_sum(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
-    v = bit_cast<float>(a[0]) + bit_cast<float>(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(bit_cast<uint32_t>(v), bit_cast<uint32_t>(v), false, false);
-    return bit_cast<float>(b[0]) + bit_cast<float>(b[1]);
+    float a, b;
+    lane_swap16(v, a, b);
+    lane_swap32(a + b, a, b);
+    return a + b;
 }
 
 }  // namespace splash

@@ -8,33 +8,34 @@
 // every page across the query heads of its group and all verify tokens (same
 // summary, section "Metal kernels generated to shape"; bnskd.com, "Tech core 2").
 //
-// Work decomposition.  One workgroup (4 waves, one per SIMD) per (request b,
-// kv head g, context split s).  Its rows are the R = G * d query rows that
-// share kv head g (G = Hq / Hkv heads times d drafts), ordered r = t * G + hh so
-// that a shorter draft truncates a prefix of rows; rows are padded to tiles of
-// 16 and the number of tiles in use is a compile-time parameter of the body.
-//  * Q is loaded once and kept in accumulation registers (AGPRs) of every wave,
-//    laid out as the B operand of 16x16x32 bf16 MFMAs (6 tiles x 8 blocks = 192
-//    registers at D = 256, G = 6, 16 drafts).
+// Work decomposition.  One workgroup of 8 waves (two per SIMD, so that each
+// SIMD always has a second wave to issue from) per (request b, kv head g,
+// context split s).  Its rows are the R = G * d query rows that share kv head
+// g, ordered r = t * G + hh so that a shorter draft truncates a prefix of rows,
+// padded to tiles of 16; the tile count in use is a compile-time parameter of
+// the body.  The 8 waves are two row halves (half h owns tiles h, h+2, h+4)
+// times four: wave (h, w) computes scores for page w of each step and owns
+// head-dim quarter w of the output, for the rows of half h.
+//  * Q is loaded once, converted bf16 -> fp16 (exact for 2^-17 <= |q| <= 65504)
+//    and kept in registers as the B operand of 16x16x32 fp16 MFMAs.
 //  * The context is walked in steps of kPagesPerIter = 4 pages (64 tokens).
-//    Wave w copies page w of a step -- K (4 KB), V (4 KB) and its 32 scales --
-//    from HBM straight into LDS with 16-byte direct-to-LDS loads, kStages - 1
-//    steps ahead of the step being computed, so the copies for two future steps
-//    are in flight while one is consumed.  K rows are XOR-swizzled by 16-byte
-//    chunk through the per-lane source address, which makes the MFMA operand
-//    reads free of bank conflicts; V pages are already stored as two d-major
-//    tiles of 8 tokens, which gives the same property with a verbatim copy.
-//  * Wave w computes S^T = K Q^T for page w (16 keys x R rows).  int8 codes x
-//    are converted exactly: byte u = x + 128 becomes fp32 then bf16 (exact for
-//    0..255), and the bias is removed per row after the MFMA:
-//        sum_d q_d x_d = sum_d q_d u_d - 128 * sum_d q_d.
-//    The K scale and the softmax scale (in log2 units) are applied in fp32.
-//  * The per-row maximum over the step's 64 keys is exchanged through LDS; each
-//    wave computes p = exp2(z - m) for its keys, folds the V scale in fp32
-//    (P' = p * s_v) and writes P' as fp16 to LDS in the B-operand layout.
-//  * Each wave then owns a quarter of the head dimension and accumulates
-//    O^T += V^T P'^T over all 64 keys with 16x16x32 fp16 MFMAs; V codes are
-//    exact in fp16 (binary16 0x64uu is 1024 + u; subtracting 1152 leaves x).
+//    Pages are copied HBM -> LDS with 16-byte direct-to-LDS loads into a ring
+//    of kStages steps, two steps ahead of their use; half 0 copies the K pages
+//    and the scales, half 1 the V pages.  K rows are XOR-swizzled by 16-byte
+//    chunk through the per-lane source address, which keeps the MFMA operand
+//    reads free of bank conflicts; V pages are stored as two d-major tiles of 8
+//    tokens, which gives the same property with a verbatim copy.
+//  * int8 codes x become fp16 with one byte permute: binary16 0x64uu is
+//    1024 + u, and u = x + 128, so the operand holds 1152 + x exactly.  For K the
+//    bias is removed per row after the MFMA (sum_d q_d (1152 + x_d) - 1152 *
+//    sum_d q_d); for V it is subtracted exactly with a packed fp16 add.
+//  * Per step: S^T = K Q^T for the wave's page; scaled scores (K scale and
+//    softmax scale in log2 units, fp32); row maxima exchanged in LDS among the
+//    half's four waves; p = exp2(z - m) against a lazily moved reference m;
+//    P' = p * s_v written as fp16 to LDS; then O^T += V^T P'^T for the wave's
+//    head-dim quarter over the step's 64 keys.  The P V product of a step runs
+//    after the next step's Q K^T, inside the same barrier interval, so each
+//    step needs two workgroup barriers.
 //  * The epilogue divides by the row sums and writes bf16 rows (one split) or
 //    fp32 partial rows plus their natural-log log-sum-exp (several splits).
 #include <math.h>
@@ -44,17 +45,36 @@
 
 namespace splash {
 
-constexpr int kStages = 3;     // LDS ring of page steps: one consumed, two in flight
+constexpr int kStages = 4;     // LDS ring of page steps (two ahead, one in Q K^T, one in P V)
+constexpr int kWaves = 8;      // two row halves x four
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) const void* global_cvoid_ptr;
 
-// Direct-to-LDS loads: lane i's 16 (or 4) bytes land at lds + 16 * i (4 * i).
-__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds) {
-    __builtin_amdgcn_global_load_lds((global_cvoid_ptr)src, (lds_void_ptr)lds, 16, 0, 0);
+// 32-bit LDS address of a pointer into the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_void_ptr)(p);
 }
-__device__ __forceinline__ void dma4_to_lds(const void* src, void* lds) {
-    __builtin_amdgcn_global_load_lds((global_cvoid_ptr)src, (lds_void_ptr)lds, 4, 0, 0);
+
+// Direct-to-LDS loads: lane i's 16 (or 4) bytes land at LDS address
+// m0 + 16 * i (4 * i).  Issued as inline assembly so that the compiler adds no
+// wait of its own: these copies are waited for explicitly (wait_vmcnt) before
+// the barrier that publishes a stage.  `lds` must be uniform in the wave.
+// Ordering: volatile asm statements keep their order, and the barrier and
+// wait statements carry the memory clobber that orders the LDS reads.
+__device__ __forceinline__ void dma16_to_lds(const void* src, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds));
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds));
+}
+
+// Block-table entry through the scalar cache (the table is read-only here).
+// As a plain C++ load the compiler would use a vector load whose wait also
+// drains the in-flight page copies.
+__device__ __forceinline__ int load_page_id(const int32_t* p) {
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    return v;
 }
 
 template <int N>
@@ -68,42 +88,29 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16 int8 codes (4 dwords) -> two bf16x8 operands holding code + 128 exactly.
-__device__ __forceinline__ uint32_t pack_bf16_bytes(uint32_t u, int hi) {
-    const float f0 = (float)((u >> (16 * hi)) & 0xffu);
-    const float f1 = (float)((u >> (16 * hi + 8)) & 0xffu);
-    // upper halves of the two fp32 values: exact bf16 because the integers fit 8 bits
-    return __builtin_amdgcn_perm(bit_cast<uint32_t>(f1), bit_cast<uint32_t>(f0), 0x07060302u);
+// Codes 0-1 (sel 0) or 2-3 (sel 1) of a dword -> two fp16 values 1152 + code.
+__device__ __forceinline__ uint32_t codes2_to_f16_biased(uint32_t raw, int sel) {
+    const uint32_t u = raw ^ 0x80808080u;
+    return __builtin_amdgcn_perm(0x64646464u, u, sel ? 0x04030402u : 0x04010400u);
 }
 
-__device__ __forceinline__ void codes16_to_bf16_biased(const u32x4_t raw, bf16x8_t& lo, bf16x8_t& hi) {
-    u32x4_t a, b;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t u = raw[w] ^ 0x80808080u;
-        a[2 * w] = pack_bf16_bytes(u, 0);
-        a[2 * w + 1] = pack_bf16_bytes(u, 1);
-        const uint32_t v = raw[w + 2] ^ 0x80808080u;
-        b[2 * w] = pack_bf16_bytes(v, 0);
-        b[2 * w + 1] = pack_bf16_bytes(v, 1);
-    }
-    lo = bit_cast<bf16x8_t>(a);
-    hi = bit_cast<bf16x8_t>(b);
+// 16 codes -> two fp16x8 operands holding 1152 + code.
+__device__ __forceinline__ void codes16_to_f16_biased(const u32x4_t raw, f16x8_t& lo, f16x8_t& hi) {
+    const u32x4_t a = {codes2_to_f16_biased(raw[0], 0), codes2_to_f16_biased(raw[0], 1),
+                       codes2_to_f16_biased(raw[1], 0), codes2_to_f16_biased(raw[1], 1)};
+    const u32x4_t b = {codes2_to_f16_biased(raw[2], 0), codes2_to_f16_biased(raw[2], 1),
+                       codes2_to_f16_biased(raw[3], 0), codes2_to_f16_biased(raw[3], 1)};
+    lo = bit_cast<f16x8_t>(a);
+    hi = bit_cast<f16x8_t>(b);
 }
 
-// 8 int8 codes -> fp16x8 holding the codes exactly.
+// 8 codes -> fp16x8 holding the codes exactly (the 1152 bias subtracted).
 __device__ __forceinline__ f16x8_t codes8_to_f16(const u32x2_t raw) {
-    const uint32_t magic = 0x64646464u;
     const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
     u32x4_t h;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const uint32_t u = raw[w] ^ 0x80808080u;
-        const f16x2_t e0 = bit_cast<f16x2_t>(__builtin_amdgcn_perm(magic, u, 0x04010400u)) - bias;
-        const f16x2_t e1 = bit_cast<f16x2_t>(__builtin_amdgcn_perm(magic, u, 0x04030402u)) - bias;
-        h[2 * w] = bit_cast<uint32_t>(e0);
-        h[2 * w + 1] = bit_cast<uint32_t>(e1);
-    }
+    for (int k = 0; k < 4; ++k)
+        h[k] = bit_cast<uint32_t>(bit_cast<f16x2_t>(codes2_to_f16_biased(raw[k >> 1], k & 1)) - bias);
     return bit_cast<f16x8_t>(h);
 }
 
@@ -119,18 +126,21 @@ struct Arena {
     static constexpr int v_off(int j) { return kPagesPerIter * PAGE + j * PAGE; }
     static constexpr int s_off(int j) { return 2 * kPagesPerIter * PAGE + j * SCALES; }
     static constexpr int NT = G;                              // row tiles for up to 16 drafts
-    static constexpr int P_OFF = kStages * STAGE;             // P'^T operand tiles, fp16
-    static constexpr int P_BYTES = (kPagesPerIter / 2) * NT * 64 * 16;
-    static constexpr int RED_OFF = P_OFF + P_BYTES;           // [row][wave] fp32 row maxima / sums,
-    static constexpr int TOTAL = RED_OFF + (NT * 16 + 1) * 4 * 4;   // then [wave] page V-scale maxima
+    static constexpr int NTH = (NT + 1) / 2;                  // row tiles per half
+    static constexpr int P_OFF = kStages * STAGE;             // two buffers of P'^T operand tiles, fp16
+    static constexpr int P_BUF = 2 * (kPagesPerIter / 2) * NTH * 64 * 16;   // [half][kb2][tile][lane][16 B]
+    static constexpr int RED_OFF = P_OFF + 2 * P_BUF;         // [row][page] fp32 maxima / sums,
+    static constexpr int TOTAL = RED_OFF + (NT * 16 + 1) * 4 * 4;   // then [page] V-scale maxima
+    static_assert(TOTAL <= 160 * 1024, "LDS arena exceeds 160 KB");
 };
 
-template <int D, int NTU>
+template <int D>
 struct Tiles {
     static constexpr int KB = D / 32;         // contraction blocks of Q K^T
     static constexpr int CH = D / 16;         // 16-byte chunks in a K row
     static constexpr int DW = D / 4;          // head-dim columns each wave owns in P V
     static constexpr int MT = DW / 16;        // V^T tiles of 16 columns per wave
+    static constexpr int NI = kPage * D / 1024;   // 16-byte copies per lane per page
     static constexpr int SWZ_DIV = CH >= 8 ? 1 : 8 / CH;
     static constexpr int SWZ_MOD = CH >= 8 ? 8 : CH;
     static_assert(D % 64 == 0 && MT >= 1, "head dim must be a multiple of 64");
@@ -139,32 +149,35 @@ struct Tiles {
 // XOR swizzle of 16-byte chunks inside a K row, by slot.
 template <int D>
 __device__ __forceinline__ int k_swizzle(int slot) {
-    using T = Tiles<D, 1>;
-    return (slot / T::SWZ_DIV) % T::SWZ_MOD;
+    return (slot / Tiles<D>::SWZ_DIV) % Tiles<D>::SWZ_MOD;
 }
 
-// Wave `wave` copies page `pg` of kv head g into stage slot `wave`.
+// Half 0 wave w copies the K page and the scales of page w of a step into the
+// stage at LDS address `stage`; half 1 wave w copies its V page.
 template <int D, int G>
-__device__ __forceinline__ void stage_page(uint8_t* stage, int wave, int lane, const VerifyArgs& a,
+__device__ __forceinline__ void stage_page(uint32_t stage, int half, int w, int lane, const VerifyArgs& a,
                                            int page, int g) {
     using A = Arena<D, G>;
-    constexpr int CH = D / 16;
-    constexpr int NI = A::PAGE / 1024;                        // 16-byte copies per lane per page
+    using T = Tiles<D>;
     const size_t blk = (size_t)page * a.Hkv + g;
-    const int8_t* kp = a.k_pool + blk * A::PAGE;
-    const int8_t* vp = a.v_pool + blk * A::PAGE;
+    if (half == 0) {
+        const int8_t* kp = a.k_pool + blk * A::PAGE;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int c = 64 * i + lane;                          // LDS chunk of this lane
-        const int slot = c / CH, pc = c % CH;
-        const int lc = pc ^ k_swizzle<D>(slot);               // logical chunk stored there
-        dma16_to_lds(kp + slot * D + 16 * lc, stage + A::k_off(wave) + 1024 * i);
-    }
+        for (int i = 0; i < T::NI; ++i) {
+            const int c = 64 * i + lane;                      // LDS chunk of this lane
+            const int slot = c / T::CH, pc = c % T::CH;
+            const int lc = pc ^ k_swizzle<D>(slot);           // logical chunk stored there
+            dma16_to_lds(kp + slot * D + 16 * lc, stage + A::k_off(w) + 1024 * i);
+        }
+        if (lane < 16) {
+            const uint16_t* src = lane < 8 ? a.k_scale + blk * kPage + 2 * lane
+                                           : a.v_scale + blk * kPage + 2 * (lane - 8);
+            dma4_to_lds(src, stage + A::s_off(w));
+        }
+    } else {
+        const int8_t* vp = a.v_pool + blk * A::PAGE;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16_to_lds(vp + 1024 * i + 16 * lane, stage + A::v_off(wave) + 1024 * i);
-    if (lane < 16) {
-        const uint16_t* src = lane < 8 ? a.k_scale + blk * kPage + 2 * lane : a.v_scale + blk * kPage + 2 * (lane - 8);
-        dma4_to_lds(src, stage + A::s_off(wave));
+        for (int i = 0; i < T::NI; ++i) dma16_to_lds(vp + 1024 * i + 16 * lane, stage + A::v_off(w) + 1024 * i);
     }
 }
 
@@ -173,242 +186,257 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                                                const int s, const int dl, const int ctx, const int pg_begin,
                                                const int pg_end) {
     using A = Arena<D, G>;
-    using T = Tiles<D, NTU>;
+    using T = Tiles<D>;
     constexpr int KB = T::KB, DW = T::DW, MT = T::MT;
-    constexpr int NI = A::PAGE / 1024;
-    constexpr int LOADS_PER_STEP = 2 * NI + 1;                // DMA instructions per wave per step
+    constexpr int NTH = (NTU + 1) / 2;                        // tiles of this body per half
+    constexpr int LOADS_H0 = T::NI + 1, LOADS_H1 = T::NI;     // copies per wave per step
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kLn2 = 0.6931471805599453f;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave >> 2, w = wave & 3;
     const int gq = lane >> 4, li = lane & 15;
     const int rows = G * dl;
     const int Hq = a.Hq, S = a.num_splits;
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq;
     const int n_steps = (pg_end - pg_begin + kPagesPerIter - 1) / kPagesPerIter;
+    // half 1 has one tile fewer when the tile count is odd
+    const bool last_tile = (half == 0) || (NTU % 2 == 0);
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
-    // start the copies of the first kStages - 1 steps before touching Q
     auto issue_step = [&](int step) {
-        int pg = pg_begin + step * kPagesPerIter + wave;
+        int pg = pg_begin + step * kPagesPerIter + w;
         if (pg >= pg_end) pg = pg_end - 1;                    // past the split: copy a valid page, masked later
-        stage_page<D, G>(lds + (step % kStages) * A::STAGE, wave, lane, a, bt[pg], g);
+        stage_page<D, G>(lds_base + (step % kStages) * A::STAGE, half, w, lane, a, load_page_id(bt + pg), g);
     };
-#pragma unroll
-    for (int st = 0; st < kStages - 1; ++st)
-        if (st < n_steps) issue_step(st);
+    issue_step(0);
+    if (n_steps > 1) issue_step(1);
 
-    // ---- Q: B operand of S^T = K Q^T, plus the per-row sum that removes the code bias
-    bf16x8_t qf[NTU][KB];
-    float qsum[NTU];
+    // ---- Q for this half's tiles (tile i of the half is row tile half + 2 i), fp16,
+    // as the B operand of S^T = K Q^T; the per-row code bias 1152 * sum_d q_d
+    f16x8_t qf[NTH][KB];
+    float qbias[NTH];
 #pragma unroll
-    for (int nt = 0; nt < NTU; ++nt) {
-        const int row = nt * 16 + li;
-        float acc = 0.0f;
-        const bool ok = row < rows;
+    for (int i = 0; i < NTH; ++i) {
+        const int row = (half + 2 * i) * 16 + li;
+        const bool ok = row < rows && (i + 1 < NTH || last_tile);
         const int t = ok ? row / G : 0, h = g * G + (ok ? row % G : 0);
         const uint16_t* qrow = a.q + (((size_t)b * a.T_max + t) * Hq + h) * D;
+        float acc = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int d0 = 64 * (kb >> 1) + 16 * gq + 8 * (kb & 1);
             u32x4_t raw = u32x4_t{0u, 0u, 0u, 0u};
             if (ok) raw = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-            qf[nt][kb] = bit_cast<bf16x8_t>(raw);
+            f16x8_t hv;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                acc += bit_cast<float>(raw[w] << 16) + bit_cast<float>(raw[w] & 0xffff0000u);
+            for (int e = 0; e < 8; ++e) {
+                const float f = bit_cast<float>(e & 1 ? raw[e >> 1] & 0xffff0000u : raw[e >> 1] << 16);
+                hv[e] = (_Float16)f;
+                acc += (float)hv[e];
+            }
+            qf[i][kb] = hv;
         }
-        qsum[nt] = group4_sum(acc) * 128.0f;
+        qbias[i] = group4_sum(acc) * 1152.0f;
     }
-#pragma unroll
-    for (int nt = 0; nt < NTU; ++nt)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+a"(qf[nt][kb]));
 
-    float m_run[NTU], l_run[NTU];
-    f32x4_t o[MT][NTU];
+    float m_run[NTH], l_run[NTH];
+    f32x4_t o[MT][NTH];
 #pragma unroll
-    for (int nt = 0; nt < NTU; ++nt) {
-        m_run[nt] = -INFINITY;
-        l_run[nt] = 0.0f;
+    for (int i = 0; i < NTH; ++i) {
+        m_run[i] = -INFINITY;
+        l_run[i] = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) o[mt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const float zscale = a.sm_scale * kLog2e;
     float* red = reinterpret_cast<float*>(lds + A::RED_OFF);
-    _Float16* pbuf = reinterpret_cast<_Float16*>(lds + A::P_OFF);
+    // P' tiles of this half: [buf][half][kb2][tile][lane][8 fp16]
+    auto pbuf = [&](int buf, int kb2, int i) {
+        return reinterpret_cast<_Float16*>(lds + A::P_OFF + buf * A::P_BUF) +
+               (((half * (kPagesPerIter / 2) + kb2) * NTH + i) * 64) * 8;
+    };
 
-    for (int step = 0; step < n_steps; ++step) {
-        // this wave's copies for `step` are done once at most the next step's remain
-        if (step + 1 < n_steps) wait_vmcnt<LOADS_PER_STEP>();
-        else wait_vmcnt<0>();
-        lds_barrier();                                        // every wave's copies visible; step-1 finished
-        if (step + kStages - 1 < n_steps) issue_step(step + kStages - 1);
-#pragma unroll
-        for (int nt = 0; nt < NTU; ++nt) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+a"(qf[nt][kb]));
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(o[mt][nt]));
+    for (int it = 0; it <= n_steps; ++it) {
+        // stage `it` copied (this wave's part) and visible to all after the barrier;
+        // also publishes P'(it - 1)
+        if (it < n_steps) {
+            if (it + 1 < n_steps) {
+                if (half == 0) wait_vmcnt<LOADS_H0>(); else wait_vmcnt<LOADS_H1>();
+            } else {
+                wait_vmcnt<0>();
+            }
         }
+        lds_barrier();
+        if (it + 2 < n_steps) issue_step(it + 2);             // into the slot of step it - 2
 
-        const uint8_t* stage = lds + (step % kStages) * A::STAGE;
-        const int pg0 = pg_begin + step * kPagesPerIter;
-        const int my_page = pg0 + wave;
-        const bool page_ok = my_page < pg_end;               // uniform in the wave
-
-        // ---- S^T = K Q^T for this wave's page
-        f32x4_t sacc[NTU];
+        // ---- P V for the previous step: O^T += V^T P'^T (this wave's head-dim quarter)
+        if (it >= 1) {
+            const int pstep = it - 1;
+            const uint8_t* pst = lds + (pstep % kStages) * A::STAGE;
+            const int ppg0 = pg_begin + pstep * kPagesPerIter;
 #pragma unroll
-        for (int nt = 0; nt < NTU; ++nt) sacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* kpage = stage + A::k_off(wave) + li * D;
-        const int swz = k_swizzle<D>(li);
+            for (int kb2 = 0; kb2 < kPagesPerIter / 2; ++kb2) {
+                if (ppg0 + 2 * kb2 < pg_end) {                // uniform
+                    f16x8_t pf[NTH];
 #pragma unroll
-        for (int c = 0; c < KB / 2; ++c) {
-            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kpage + 16 * ((4 * c + gq) ^ swz));
-            bf16x8_t k0, k1;
-            codes16_to_bf16_biased(raw, k0, k1);
+                    for (int i = 0; i < NTH; ++i)
+                        pf[i] = *reinterpret_cast<const f16x8_t*>(pbuf(pstep & 1, kb2, i) + lane * 8);
+                    // lane group gq holds keys of page 2*kb2 + gq/2, tile gq&1 (slots 8*(gq&1)..+7)
+                    const uint8_t* vt = pst + A::v_off(2 * kb2 + (gq >> 1)) + (gq & 1) * (D * 8);
 #pragma unroll
-            for (int nt = 0; nt < NTU; ++nt) {
-                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[nt][2 * c], sacc[nt], 0, 0, 0);
-                sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[nt][2 * c + 1], sacc[nt], 0, 0, 0);
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const int d = w * DW + mt * 16 + li;
+                        const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vt + d * 8));
+#pragma unroll
+                        for (int i = 0; i < NTH; ++i)
+                            o[mt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[i], o[mt][i], 0, 0, 0);
+                    }
+                }
             }
         }
 
-        // ---- scaled scores (masked only on pages that are not fully visible)
-        // lane (gq, li) holds keys at slots 4*gq + j of page my_page, for row 16*nt + li
-        const u32x2_t ks_raw = *reinterpret_cast<const u32x2_t*>(stage + A::s_off(wave) + 8 * gq);
-        const u32x2_t vs_raw = *reinterpret_cast<const u32x2_t*>(stage + A::s_off(wave) + 32 + 8 * gq);
+        // ---- Q K^T for this step's page w and this half's tiles
+        f32x4_t sacc[NTH];
         float kc[4], vsc[4];
+        bool all_visible = false;
+        const int pg0 = pg_begin + it * kPagesPerIter;
+        const int my_page = pg0 + w;
+        const bool page_ok = my_page < pg_end;               // uniform in the wave
+        if (it < n_steps) {
+            const uint8_t* stage = lds + (it % kStages) * A::STAGE;
+            const uint8_t* kpage = stage + A::k_off(w) + li * D;
+            const int swz = k_swizzle<D>(li);
+            u32x4_t kraw[KB / 2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kc[j] = f16_bits_to_f32(ks_raw[j >> 1] >> (16 * (j & 1))) * zscale;
-            vsc[j] = f16_bits_to_f32(vs_raw[j >> 1] >> (16 * (j & 1)));
-        }
-        // every key of the page is visible to every row (padded rows see q = 0)
-        const bool all_visible = page_ok && my_page * kPage + kPage - 1 <= ctx - dl;
-        if (all_visible) {
+            for (int c = 0; c < KB / 2; ++c)
+                kraw[c] = *reinterpret_cast<const u32x4_t*>(kpage + 16 * ((4 * c + gq) ^ swz));
 #pragma unroll
-            for (int nt = 0; nt < NTU; ++nt) {
-                float mx = -INFINITY;
+            for (int i = 0; i < NTH; ++i) sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sacc[nt][j] = (sacc[nt][j] - qsum[nt]) * kc[j];
-                    mx = fmaxf(mx, sacc[nt][j]);
+            for (int c = 0; c < KB / 2; ++c) {
+                f16x8_t k0, k1;
+                codes16_to_f16_biased(kraw[c], k0, k1);
+#pragma unroll
+                for (int i = 0; i < NTH; ++i) {
+                    sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[i][2 * c], sacc[i], 0, 0, 0);
+                    sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[i][2 * c + 1], sacc[i], 0, 0, 0);
                 }
-                mx = group4_max(mx);
-                if (gq == 0) red[(nt * 16 + li) * 4 + wave] = mx;
             }
-        } else {
-            const int key0 = my_page * kPage + 4 * gq;
+            // lane (gq, li) holds keys at slots 4*gq + j of page my_page, for row 16*tile + li
+            const u32x2_t ks_raw = *reinterpret_cast<const u32x2_t*>(stage + A::s_off(w) + 8 * gq);
+            const u32x2_t vs_raw = *reinterpret_cast<const u32x2_t*>(stage + A::s_off(w) + 32 + 8 * gq);
 #pragma unroll
-            for (int nt = 0; nt < NTU; ++nt) {
-                const int row = nt * 16 + li;
-                const int pos_t = ctx - dl + row / G;         // last key this row may see
-                const bool row_ok = page_ok && row < rows;
-                float mx = -INFINITY;
+            for (int j = 0; j < 4; ++j) {
+                kc[j] = f16_bits_to_f32(ks_raw[j >> 1] >> (16 * (j & 1))) * zscale;
+                vsc[j] = f16_bits_to_f32(vs_raw[j >> 1] >> (16 * (j & 1)));
+            }
+            // every key of the page is visible to every row (padded rows see q = 0)
+            all_visible = page_ok && my_page * kPage + kPage - 1 <= ctx - dl;
+            float rmax[NTH];
+            if (all_visible) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float zz = (sacc[nt][j] - qsum[nt]) * kc[j];
-                    sacc[nt][j] = (row_ok && key0 + j <= pos_t) ? zz : -INFINITY;
-                    mx = fmaxf(mx, sacc[nt][j]);
+                for (int i = 0; i < NTH; ++i) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sacc[i][j] = (sacc[i][j] - qbias[i]) * kc[j];
+                        mx = fmaxf(mx, sacc[i][j]);
+                    }
+                    rmax[i] = group4_max(mx);
                 }
-                mx = group4_max(mx);
-                if (gq == 0) red[row * 4 + wave] = mx;
+            } else {
+                const int key0 = my_page * kPage + 4 * gq;
+#pragma unroll
+                for (int i = 0; i < NTH; ++i) {
+                    const int row = (half + 2 * i) * 16 + li;
+                    const int pos_t = ctx - dl + row / G;     // last key this row may see
+                    const bool row_ok = page_ok && row < rows;
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float zz = (sacc[i][j] - qbias[i]) * kc[j];
+                        sacc[i][j] = (row_ok && key0 + j <= pos_t) ? zz : -INFINITY;
+                        mx = fmaxf(mx, sacc[i][j]);
+                    }
+                    rmax[i] = group4_max(mx);
+                }
             }
-        }
-        // largest V scale of this page (masked slots included: a non-finite or
-        // huge value only makes the rescaling below exact)
-        {
-            float vm = fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3]));
-            vm = group4_max(vm);
-            if (lane == 0) red[A::NT * 16 * 4 + wave] = vm;
+            // largest V scale of the page (masked slots included: a non-finite or
+            // huge value only makes the rescaling below exact)
+            const float vmax = group4_max(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])));
+            if (gq == 0) {
+#pragma unroll
+                for (int i = 0; i < NTH; ++i) red[((half + 2 * i) * 16 + li) * 4 + w] = rmax[i];
+                if (li == 0 && half == 0) red[A::NT * 16 * 4 + w] = vmax;
+            }
         }
         lds_barrier();
 
-        // ---- online softmax with a lazily moved reference.  The reference m of a
-        // row only moves when the step's maximum exceeds it by more than tau (log2
+        // ---- online softmax with a lazily moved reference.  A row's reference m
+        // only moves when the step's maximum exceeds it by more than tau (log2
         // units), so p = exp2(z - m) <= 2^tau; tau = 8 unless a V scale of the
         // step exceeds 255, where P' = p * s_v could leave the fp16 range, and then
         // tau = 0 (the reference follows the maximum exactly).
-        const f32x4_t vsm = *reinterpret_cast<const f32x4_t*>(red + A::NT * 16 * 4);
-        const float tau = (fmaxf(fmaxf(vsm[0], vsm[1]), fmaxf(vsm[2], vsm[3])) <= 255.0f) ? 8.0f : 0.0f;
-        _Float16* p_dst = pbuf + (((wave >> 1) * NTU) * 64 + (2 * (wave & 1) + (gq >> 1)) * 16 + li) * 8
-                          + 4 * (gq & 1);
+        if (it < n_steps) {
+            const f32x4_t vsm = *reinterpret_cast<const f32x4_t*>(red + A::NT * 16 * 4);
+            const float tau = (fmaxf(fmaxf(vsm[0], vsm[1]), fmaxf(vsm[2], vsm[3])) <= 255.0f) ? 8.0f : 0.0f;
 #pragma unroll
-        for (int nt = 0; nt < NTU; ++nt) {
-            const int row = nt * 16 + li;
-            const f32x4_t mw = *reinterpret_cast<const f32x4_t*>(red + row * 4);
-            const float mstep = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-            const bool move = mstep > m_run[nt] + tau;       // -inf + tau stays -inf
-            const float alpha = move ? __builtin_amdgcn_exp2f(m_run[nt] - mstep) : 1.0f;
-            if (move) m_run[nt] = mstep;
-            if (__builtin_amdgcn_ballot_w64(move) != 0) {     // some row of the tile moved
-                l_run[nt] *= alpha;
+            for (int i = 0; i < NTH; ++i) {
+                const int row = (half + 2 * i) * 16 + li;
+                const f32x4_t mw = *reinterpret_cast<const f32x4_t*>(red + row * 4);
+                const float mstep = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+                const bool move = mstep > m_run[i] + tau;     // -inf + tau stays -inf
+                const float alpha = move ? __builtin_amdgcn_exp2f(m_run[i] - mstep) : 1.0f;
+                if (move) m_run[i] = mstep;
+                if (__builtin_amdgcn_ballot_w64(move) != 0) { // some row of the tile moved
+                    l_run[i] *= alpha;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
-            }
-            // rows that have seen no key yet keep m = -inf; their scores are all -inf
-            const float mref = m_run[nt] == -INFINITY ? 0.0f : m_run[nt];
-            float psum = 0.0f;
-            _Float16 ph[4];
-            if (all_visible) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[nt][j] - mref);
-                    psum += p;
-                    ph[j] = (_Float16)(p * vsc[j]);
+                    for (int mt = 0; mt < MT; ++mt) o[mt][i] *= alpha;
                 }
-            } else {
+                // rows that have seen no key yet keep m = -inf; their scores are all -inf
+                const float mref = m_run[i] == -INFINITY ? 0.0f : m_run[i];
+                float psum = 0.0f;
+                _Float16 ph[4];
+                if (all_visible) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[nt][j] - mref);   // exp2(-inf) = 0
-                    psum += p;
-                    ph[j] = (_Float16)(sacc[nt][j] != -INFINITY ? p * vsc[j] : 0.0f);
+                    for (int j = 0; j < 4; ++j) {
+                        const float p = __builtin_amdgcn_exp2f(sacc[i][j] - mref);
+                        psum += p;
+                        ph[j] = (_Float16)(p * vsc[j]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float p = __builtin_amdgcn_exp2f(sacc[i][j] - mref);   // exp2(-inf) = 0
+                        psum += p;
+                        ph[j] = (_Float16)(sacc[i][j] != -INFINITY ? p * vsc[j] : 0.0f);
+                    }
                 }
-            }
-            l_run[nt] += psum;                                // this lane's share of the row sum
-            u32x2_t packed;
-            packed[0] = (uint32_t)bit_cast<uint16_t>(ph[0]) | ((uint32_t)bit_cast<uint16_t>(ph[1]) << 16);
-            packed[1] = (uint32_t)bit_cast<uint16_t>(ph[2]) | ((uint32_t)bit_cast<uint16_t>(ph[3]) << 16);
-            *reinterpret_cast<u32x2_t*>(p_dst + nt * 64 * 8) = packed;
-        }
-        lds_barrier();
-
-        // ---- O^T += V^T P'^T over the step's keys, for this wave's head-dim quarter
-#pragma unroll
-        for (int kb2 = 0; kb2 < kPagesPerIter / 2; ++kb2) {
-            if (pg0 + 2 * kb2 < pg_end) {                    // uniform
-                f16x8_t pf[NTU];
-#pragma unroll
-                for (int nt = 0; nt < NTU; ++nt)
-                    pf[nt] = *reinterpret_cast<const f16x8_t*>(pbuf + ((kb2 * NTU + nt) * 64 + lane) * 8);
-                // lane group gq holds keys of page 2*kb2 + gq/2, tile (slots 8*(gq&1)..+7)
-                const uint8_t* vt = stage + A::v_off(2 * kb2 + (gq >> 1)) + (gq & 1) * (D * 8);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const int d = wave * DW + mt * 16 + li;
-                    const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vt + d * 8));
-#pragma unroll
-                    for (int nt = 0; nt < NTU; ++nt)
-                        o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[nt], o[mt][nt], 0, 0, 0);
-                }
+                l_run[i] += psum;                             // this lane's share of the row sum
+                // reader lane (group 2*(w&1) + gq/2, li) of block kb2 = w/2 holds 8 keys;
+                // these 4 are its elements 4*(gq&1)..+3
+                u32x2_t packed;
+                packed[0] = (uint32_t)bit_cast<uint16_t>(ph[0]) | ((uint32_t)bit_cast<uint16_t>(ph[1]) << 16);
+                packed[1] = (uint32_t)bit_cast<uint16_t>(ph[2]) | ((uint32_t)bit_cast<uint16_t>(ph[3]) << 16);
+                *reinterpret_cast<u32x2_t*>(pbuf(it & 1, w >> 1, i) + ((2 * (w & 1) + (gq >> 1)) * 16 + li) * 8 +
+                                            4 * (gq & 1)) = packed;
             }
         }
     }
 
-    // ---- epilogue: row sums across lane groups and waves, then normalise
-    lds_barrier();
+    // ---- epilogue: row sums across lane groups and the half's four waves, then normalise
 #pragma unroll
-    for (int nt = 0; nt < NTU; ++nt) {
-        const float l = group4_sum(l_run[nt]);
-        if (gq == 0) red[(nt * 16 + li) * 4 + wave] = l;
+    for (int i = 0; i < NTH; ++i) {
+        const float l = group4_sum(l_run[i]);
+        if (gq == 0) red[((half + 2 * i) * 16 + li) * 4 + w] = l;
     }
     lds_barrier();
 #pragma unroll
-    for (int nt = 0; nt < NTU; ++nt) {
-        const int row = nt * 16 + li;
-        if (row >= rows) continue;
+    for (int i = 0; i < NTH; ++i) {
+        const int row = (half + 2 * i) * 16 + li;
+        if (row >= rows || !(i + 1 < NTH || last_tile)) continue;
         const f32x4_t lw = *reinterpret_cast<const f32x4_t*>(red + row * 4);
         const float l = (lw[0] + lw[1]) + (lw[2] + lw[3]);
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -417,24 +445,24 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             uint16_t* orow = a.out + (((size_t)b * a.T_max + t) * Hq + h) * D;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int d = wave * DW + mt * 16 + 4 * gq;
-                u32x2_t w;
-                w[0] = (uint32_t)f32_to_bf16_rne(o[mt][nt][0] * inv) |
-                       ((uint32_t)f32_to_bf16_rne(o[mt][nt][1] * inv) << 16);
-                w[1] = (uint32_t)f32_to_bf16_rne(o[mt][nt][2] * inv) |
-                       ((uint32_t)f32_to_bf16_rne(o[mt][nt][3] * inv) << 16);
-                *reinterpret_cast<u32x2_t*>(orow + d) = w;
+                const int d = w * DW + mt * 16 + 4 * gq;
+                u32x2_t v;
+                v[0] = (uint32_t)f32_to_bf16_rne(o[mt][i][0] * inv) |
+                       ((uint32_t)f32_to_bf16_rne(o[mt][i][1] * inv) << 16);
+                v[1] = (uint32_t)f32_to_bf16_rne(o[mt][i][2] * inv) |
+                       ((uint32_t)f32_to_bf16_rne(o[mt][i][3] * inv) << 16);
+                *reinterpret_cast<u32x2_t*>(orow + d) = v;
             }
         } else {
             const size_t prow = (((size_t)b * Hq + h) * a.T_max + t) * S + s;
             float* po = a.part_o + prow * D;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int d = wave * DW + mt * 16 + 4 * gq;
-                *reinterpret_cast<f32x4_t*>(po + d) = o[mt][nt] * inv;
+                const int d = w * DW + mt * 16 + 4 * gq;
+                *reinterpret_cast<f32x4_t*>(po + d) = o[mt][i] * inv;
             }
-            if (wave == 0 && gq == 0)
-                a.part_lse[prow] = l > 0.0f ? (m_run[nt] + log2f(l)) * kLn2 : -INFINITY;
+            if (w == 0 && gq == 0)
+                a.part_lse[prow] = l > 0.0f ? (m_run[i] + log2f(l)) * kLn2 : -INFINITY;
         }
     }
 }
@@ -453,7 +481,7 @@ __device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a,
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 1) void verify_partition_kernel(const VerifyArgs a) {
+__global__ __launch_bounds__(kWaves * 64) void verify_partition_kernel(const VerifyArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[Arena<D, G>::TOTAL];
 
     // work item: blockIdx.x = (b * Hkv + g) * S + s  (equal (g, s) of different
@@ -472,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void verify_partition_kernel(const VerifyAr
     const int pg_end = min(pg_begin + a.pages_per_split, n_pages);
     const int rows = G * dl;
     if (pg_begin >= pg_end) {                                 // empty split: mark it, write no row
-        for (int r = threadIdx.x; r < rows; r += 256) {
+        for (int r = threadIdx.x; r < rows; r += kWaves * 64) {
             const int t = r / G, h = g * G + r % G;
             a.part_lse[(((size_t)b * a.Hq + h) * a.T_max + t) * S + s] = -INFINITY;
         }
@@ -482,12 +510,19 @@ __global__ __launch_bounds__(256, 1) void verify_partition_kernel(const VerifyAr
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of S context splits: one wave per output row.
+// Log-sum-exp merge of S context splits.  One workgroup (4 waves) per output
+// row: wave w accumulates splits s = w, w + 4, ... (eight loads in flight per
+// lane), then the four partial sums are added in wave order -- a fixed order,
+// so the result is deterministic.
 // ---------------------------------------------------------------------------
+constexpr int kMergeWaves = 4;
+constexpr int kMergeUnroll = 8;
+
 template <int D>
-__global__ __launch_bounds__(64) void splitk_merge_kernel(const MergeArgs a) {
+__global__ __launch_bounds__(256) void splitk_merge_kernel(const MergeArgs a) {
     constexpr int E = D / 64;
-    const int lane = threadIdx.x;
+    __shared__ float part[kMergeWaves - 1][D];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.x % a.Hq;
     const int bt = blockIdx.x / a.Hq;
     const int t = bt % a.T_max;
@@ -498,29 +533,57 @@ __global__ __launch_bounds__(64) void splitk_merge_kernel(const MergeArgs a) {
     const float* lse = a.part_lse + prow;
     float M = -INFINITY;
     for (int s = lane; s < S; s += 64) M = fmaxf(M, lse[s]);
-    M = wave_max(M);
+    M = wave_max(M);                                          // identical in every wave
+    float W = 0.0f;                                           // identical in every lane: same order
+    for (int s = 0; s < S; ++s) {
+        const float l = lse[s];
+        if (l != -INFINITY) W += expf(l - M);
+    }
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    float W = 0.0f;
-    for (int s = 0; s < S; ++s) {                             // ascending s: deterministic
-        const float l = lse[s];
-        if (l == -INFINITY) continue;                         // empty split: its row is never read
-        const float w = expf(l - M);
-        W += w;
-        const float* src = a.part_o + (prow + s) * D + lane * E;
-        if constexpr (E == 4) {
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src);
+    const float* src = a.part_o + prow * D + lane * E;
+    for (int s0 = wave; s0 < S; s0 += kMergeWaves * kMergeUnroll) {
+        float v[kMergeUnroll][E];
+        float w[kMergeUnroll];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += w * v[e];
-        } else {
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int s = s0 + u * kMergeWaves;
+            const float l = s < S ? lse[s] : -INFINITY;
+            w[u] = l == -INFINITY ? 0.0f : expf(l - M);
+            if (w[u] != 0.0f) {                               // an empty split's row is never read
+                if constexpr (E == 4) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + (size_t)s * D);
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] += w * src[e];
+                    for (int e = 0; e < 4; ++e) v[u][e] = x[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) v[u][e] = src[(size_t)s * D + e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[u][e] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += w[u] * v[u][e];
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) part[wave - 1][lane * E + e] = acc[e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float x = acc[e];
+#pragma unroll
+            for (int w2 = 0; w2 < kMergeWaves - 1; ++w2) x += part[w2][lane * E + e];
+            a.out[(((size_t)b * a.T_max + t) * a.Hq + h) * D + lane * E + e] = f32_to_bf16_rne(x / W);
         }
     }
-    uint16_t* dst = a.out + (((size_t)b * a.T_max + t) * a.Hq + h) * D + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) dst[e] = f32_to_bf16_rne(acc[e] / W);
 }
 
 // ---------------------------------------------------------------------------
@@ -533,7 +596,7 @@ static hipError_t launch_partition_dg(const VerifyArgs& a, hipStream_t stream) {
     const long blocks = (long)a.B * a.Hkv * a.num_splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((verify_partition_kernel<D, G>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((verify_partition_kernel<D, G>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -550,9 +613,9 @@ hipError_t launch_splitk_merge(const MergeArgs& a, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     switch (a.D) {
-        case 64: hipLaunchKernelGGL((splitk_merge_kernel<64>), dim3((unsigned)blocks), dim3(64), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((splitk_merge_kernel<128>), dim3((unsigned)blocks), dim3(64), 0, stream, a); break;
-        case 256: hipLaunchKernelGGL((splitk_merge_kernel<256>), dim3((unsigned)blocks), dim3(64), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((splitk_merge_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((splitk_merge_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, stream, a); break;
+        case 256: hipLaunchKernelGGL((splitk_merge_kernel<256>), dim3((unsigned)blocks), dim3(256), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
