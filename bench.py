@@ -13,16 +13,31 @@ HBM before timing.  Steps rotate over R disjoint replicas of the request's
 pages (identical values, R * 67 MB >= 1 GiB) so that the 256 MB Infinity
 Cache cannot serve the context from one step to the next.
 
+Timing.  Each step is a captured HIP graph (one per replica).  The timed
+replays are queued behind a device-side sleep, so the GPU runs them back to
+back whatever the host's launch rate; events on the launch stream bracket
+exactly K steps.  The partition kernel is also timed alone, K launches back to
+back between one event pair (queued the same way): its algorithmic bytes over
+its mean launch duration give `roofline.achieved`.
+
 Prints one JSON line.  `value` is the step's algorithmic HBM bytes (int8 K and
 V plus fp16 scales per context token and kv head, q in, out, block table and
 lengths, and the append's source rows, codes and scales) over the step time.
-`roofline` is the verify partition kernel alone: its algorithmic bytes over its
-mean launch duration measured with HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle on the host cores on a bounded sample.
+`roofline.traffic` is the partition kernel's measured HBM bytes per launch,
+taken from the committed counter summary when that summary was made from the
+kernel source now in the tree (else null).  `cpu_baseline` times the CPU
+oracle on the host cores.
+
+Host-only helper modes (no GPU) turn rocprofv3 CSV output into the short text
+summaries kept under profiles/:
+    python bench.py --summarize-stats DIR CMD...
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR CMD...
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +52,13 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0
 METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak) at 32K ctx, T=16"
 WORKLOAD = "verify 1 req x ctx 32768, T=16 drafts, 24q/4kv heads, D=256, int8 KV in 16-token pages"
+PART_KERNEL = "verify_partition_kernel"
+TRAFFIC_SUMMARY = ROOT / "profiles" / "verify_partition_d256_ctx32k_hbm_traffic.md"
+# sources the partition kernel is compiled from (their hash stamps counter summaries)
+KERNEL_SOURCES = ["speculative_decode_attention_amd/csrc/verify_attn.hip",
+                  "speculative_decode_attention_amd/csrc/device.h",
+                  "speculative_decode_attention_amd/csrc/launch.h"]
+CALIB_MIB = 512
 
 
 def parse():
@@ -47,7 +69,12 @@ def parse():
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's preset")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle rows timed for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat whole oracle calls until this much wall time has passed")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run a plain {CALIB_MIB} MiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
+    ap.add_argument("--summarize-traffic", nargs="+", metavar="ARG")
     return ap.parse_args()
 
 
@@ -64,8 +91,32 @@ def append_bytes(T, Hkv, D, B=1):
     return B * T * Hkv * (2 * D * 4 + 2 * D + 2 * 2) + 8 * B
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """Measured HBM bytes per partition launch from the committed counter summary,
+    if it was made from the kernel source now in the tree."""
+    if not TRAFFIC_SUMMARY.exists():
+        return None
+    for line in TRAFFIC_SUMMARY.read_text().splitlines():
+        if line.startswith("{") and '"source_hash"' in line:
+            rec = json.loads(line)
+            if rec.get("source_hash") == kernel_source_hash():
+                return rec
+    return None
+
+
 def main():
     args = parse()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats[0], args.summarize_stats[1:])
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic[:2], args.summarize_traffic[2:])
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sharding by request, kv head or context is described in DESIGN.md).", file=sys.stderr)
@@ -115,68 +166,99 @@ def main():
     S_req = args.splits or sda.splash_verify_attn_default_splits(B, Hkv, ctx, P, D)
     S = sda.effective_splits(ctx, P, S_req)
     ws = torch.empty(max(sda.splash_verify_attn_workspace_bytes(B, T, Hq, D, S), 16), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    def step(i):
-        bt = bts[i % R]
-        sda.splash_kv_append_int8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, bt, ctx_t, dl_t)
-        sda.splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, bt, ctx_t, dl_t, ctx,
-                               wl.sm_scale, num_splits=S_req, workspace=ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    step_bytes = verify_bytes(ctx, Hkv, D, T, Hq) + append_bytes(T, Hkv, D)
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-
-    # the verify call alone (partition + merge), rotating replicas
-    e0.record()
-    for i in range(args.steps):
-        bt = bts[i % R]
-        sda.splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, bt, ctx_t, dl_t, ctx,
-                               wl.sm_scale, num_splits=S_req, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    us_verify = e0.elapsed_time(e1) / args.steps * 1e3
-
-    # the partition kernel alone: HIP events around each launch on its stream
     part_o = torch.empty((B, Hq, T, S, D), dtype=torch.float32, device=dev)
     part_lse = torch.empty((B, Hq, T, S), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(r):
+        sda.splash_kv_append_int8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t)
+        sda.splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t, ctx,
+                               wl.sm_scale, num_splits=S_req, workspace=ws)
+
+    def verify(r):
+        sda.splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t, ctx,
+                               wl.sm_scale, num_splits=S_req, workspace=ws)
+
+    def partition(r):
+        sda.splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t,
+                                         ctx, wl.sm_scale, S, part_o, part_lse)
+
+    # one captured graph per replica; eager calls first so every lazy init is done
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    step_graphs, verify_graphs = [], []
+    for fn, graphs in ((step, step_graphs), (verify, verify_graphs)):
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fn(r)
+            graphs.append(g)
+    torch.cuda.synchronize()
+
+    def sleep_ahead(n_items):
+        # keep the GPU busy while the host queues n_items (about 40 us of host time each)
+        torch.cuda._sleep(int(max(n_items, 1) * 40e-6 * 2.0e9))
+
+    def timed_replays(graphs, n, warm):
+        for i in range(warm):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sleep_ahead(n)
+        e0.record()
+        for i in range(n):
+            graphs[i % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_step = timed_replays(step_graphs, args.steps, args.warmup)
+    step_bytes = verify_bytes(ctx, Hkv, D, T, Hq) + append_bytes(T, Hkv, D)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    us_verify = timed_replays(verify_graphs, args.steps, args.warmup) * 1e3
+
+    # the partition kernel alone, launched back to back on its stream: one event
+    # pair brackets the launches (queued behind a sleep, so the host's launch
+    # rate does not show); also an event pair around each single launch
+    for i in range(args.warmup):
+        partition(i % R)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sleep_ahead(args.steps)
+    e0.record()
+    for i in range(args.steps):
+        partition(i % R)
+    e1.record()
+    torch.cuda.synchronize()
+    part_us = e0.elapsed_time(e1) / args.steps * 1e3
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.warmup):
-        sda.splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, bts[i % R], ctx_t, dl_t,
-                                         ctx, wl.sm_scale, S, part_o, part_lse)
+    sleep_ahead(args.steps)
     for i in range(args.steps):
         starts[i].record()
-        sda.splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, bts[i % R], ctx_t, dl_t,
-                                         ctx, wl.sm_scale, S, part_o, part_lse)
+        partition(i % R)
         ends[i].record()
     torch.cuda.synchronize()
-    part_us = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e3
+    part_us_single = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e3
     part_bytes = verify_bytes(ctx, Hkv, D, T, Hq)
     achieved = part_bytes / (part_us * 1e-6) / 1e9
 
-    # MALL-warm reference: the same call on one page set
-    e0.record()
-    for i in range(args.steps):
-        sda.splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, bts[0], ctx_t, dl_t, ctx,
-                               wl.sm_scale, num_splits=S_req, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    us_warm = e0.elapsed_time(e1) / args.steps * 1e3
+    if args.copy_calibration:
+        n = CALIB_MIB * 2 ** 20 // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
 
+    trec = stored_traffic()
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -194,38 +276,124 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8",
                    "splits": S, "replicas": R, "step_bytes": step_bytes,
                    "verify_us_per_call": round(us_verify, 2),
-                   "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                   "verify_us_per_call_mall_warm": round(us_warm, 2)},
+                   "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)},
         "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel<256,6>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": part_bytes, "mean_launch_us": round(part_us, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": trec["hbm_bytes_per_launch"] if trec else None,
+                     "bytes_per_launch": part_bytes, "mean_launch_us": round(part_us, 3),
+                     "single_launch_event_us": round(part_us_single, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, n_rows):
-    """The oracle as it stands, on this host's cores, over a bounded sample of rows."""
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands, on this host's cores: whole verify calls of the
+    same workload, repeated until `seconds` of wall time have passed."""
     import oracle
     orc = oracle.load()
     pools = [a.copy() for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
     for ph in wl.appends:
         orc.kv_append_int8(ph.k_src, ph.v_src, *pools, ph.block_table, ph.context_lens, ph.draft_lens)
     rows = np.array([(0, t, h) for t in range(int(wl.draft_lens[0])) for h in range(wl.Hq)], np.int32)
-    rows = rows[:n_rows]
+    calls = 0
     t0 = time.perf_counter()
-    orc.verify_attn_rows(wl.q, *pools, wl.block_table, wl.context_lens, wl.draft_lens, wl.Hkv,
-                         wl.sm_scale, rows)
-    sec = time.perf_counter() - t0
-    total_rows = int(wl.draft_lens.sum()) * wl.Hq
+    while True:
+        orc.verify_attn_rows(wl.q, *pools, wl.block_table, wl.context_lens, wl.draft_lens, wl.Hkv,
+                             wl.sm_scale, rows)
+        calls += 1
+        sec = time.perf_counter() - t0
+        if sec >= seconds:
+            break
+    sec_per_call = sec / calls
     call_bytes = verify_bytes(int(wl.context_lens[0]), wl.Hkv, wl.D, wl.T_max, wl.Hq)
-    sec_per_call = sec * total_rows / len(rows)
-    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    return {"value": round(call_bytes / sec_per_call / 1e9, 3), "unit": "GB/s", "cores": threads,
+    return {"value": round(call_bytes / sec_per_call / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle",
-            "sample": f"{len(rows)} of {total_rows} output rows of one verify call (fp64 C oracle, "
-                      f"OpenMP), {sec:.2f} s; scaled to a whole call: {sec_per_call * 1e3:.0f} ms/call"}
+            "sample": f"{calls} whole verify calls of the benchmark workload ({len(rows)} output rows "
+                      f"each, fp64 C oracle, OpenMP) in {sec:.1f} s: {sec_per_call * 1e3:.0f} ms/call"}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (host only)
+# ---------------------------------------------------------------------------
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "")
+    if "splash::" in name:
+        return name.split("(")[0].replace("splash::", "")
+    return name[:60]
+
+
+def _find(d: str, suffix: str) -> Path:
+    hits = sorted(Path(d).rglob(f"*{suffix}"))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def summarize_stats(d, cmd):
+    """Markdown summary of a `rocprofv3 --kernel-trace --stats` run."""
+    rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
+    print("# Kernel time: verify path, 32K context, T=16, 24q/4kv heads, D=256\n")
+    print("Command (from the repository root on an MI355X):\n")
+    print("```\n" + " ".join(cmd) + "\n```\n")
+    print(f"Partition kernel source hash: `{kernel_source_hash()}`\n")
+    print("| kernel | calls | mean µs | min µs | max µs | share % |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+
+
+def _per_dispatch(d, counter):
+    per = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_traffic(fetch_dir, write_dir, cmd):
+    """HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE (KiB) passes, each
+    scaled by what the same counter reads for a plain copy of known size."""
+    fetch, write = _per_dispatch(fetch_dir, "FETCH_SIZE"), _per_dispatch(write_dir, "WRITE_SIZE")
+    calib_bytes = CALIB_MIB * 2 ** 20
+
+    def calib(per):
+        cands = [(k, v) for k, v in per.items() if "neg" in k.lower()]
+        if not cands:
+            raise SystemExit("no copy-calibration (neg) kernel in the counter output")
+        vals = max(cands, key=lambda kv: np.mean(kv[1]))[1]
+        return calib_bytes / (float(np.median(vals)) * 1024.0)
+
+    f_fac, w_fac = calib(fetch), calib(write)
+    part = [k for k in fetch if PART_KERNEL in k]
+    if not part:
+        raise SystemExit("no partition kernel in the counter output")
+    print("# HBM traffic: verify path, 32K context, T=16, 24q/4kv heads, D=256\n")
+    print("Commands (from the repository root on an MI355X), one counter per run:\n")
+    print("```\n" + " ".join(cmd) + "\n```\n")
+    print(f"Calibration: a plain {CALIB_MIB} MiB device copy (torch.neg, {calib_bytes} bytes read and "
+          f"{calib_bytes} written) reads FETCH_SIZE x {f_fac:.3f} and WRITE_SIZE x {w_fac:.3f} "
+          "of the true bytes; the figures below are scaled by these factors.\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |")
+    print("|---|---:|---:|---:|---:|---:|")
+    rec = None
+    for k in sorted(fetch):
+        if "splash::" not in k:
+            continue
+        fk, wk = float(np.mean(fetch[k])), float(np.mean(write.get(k, [0.0])))
+        fb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
+        print(f"| `{_short(k)}` | {len(fetch[k])} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+        if PART_KERNEL in k and "256" in _short(k):
+            rec = {"kernel": _short(k), "source_hash": kernel_source_hash(),
+                   "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                   "hbm_bytes_per_launch": round(fb + wb), "fetch_factor": round(f_fac, 4),
+                   "write_factor": round(w_fac, 4)}
+    print("\nRecord read by bench.py (`roofline.traffic`, only while the source hash matches):\n")
+    print(json.dumps(rec))
 
 
 if __name__ == "__main__":

@@ -53,6 +53,8 @@ def _declare(lib):
                                                  _I, _I, _I, _I, _I, _I, _I, _D, _I, _I,
                                                  _P, _P]
     lib.splash_ref_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I]
+    lib.splash_ref_num_threads.argtypes = []
+    lib.splash_ref_num_threads.restype = ctypes.c_int
     lib.ref_quantize_row.argtypes = [_P, _I, _P, _P]
     lib.ref_quantize_row.restype = None
     lib.ref_f32_to_f16_rne.argtypes = [ctypes.c_float]
@@ -78,6 +80,10 @@ class Oracle:
         return a.ctypes.data_as(ctypes.c_void_p)
 
     # -- quantiser ---------------------------------------------------------
+    def num_threads(self) -> int:
+        """Threads the oracle's parallel loops run on."""
+        return int(self.lib.splash_ref_num_threads())
+
     def f32_to_f16(self, x: float) -> int:
         return int(self.lib.ref_f32_to_f16_rne(float(x)))
 

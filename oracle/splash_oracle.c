@@ -49,6 +49,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define REF_OK 0
 #define REF_ERR_ARG 1
@@ -422,6 +425,16 @@ int splash_ref_verify_attn_split(const uint16_t* q,
  * [B][Hq][T_max][S]); arithmetic and out ([B][T_max][Hq][D]) are fp64.
  * Rows t >= draft_lens[b] are left untouched.
  */
+/* Threads the OpenMP loops of this library use (1 when built without OpenMP). */
+int splash_ref_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 int splash_ref_splitk_merge(const float* part_o, const float* part_lse, double* out,
                             const int32_t* draft_lens, int B, int T_max, int Hq, int D,
                             int num_splits)
