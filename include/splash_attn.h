@@ -43,10 +43,15 @@
  *      ceil(context_lens[b] / P) <= max_pages_per_seq
  *      every block_table entry that is used lies in [0, num_pages)
  *      appended positions never land in a page another request shares
+ *      every finite query element has |q| <= 65504 (verify multiplies q in
+ *      binary16; elements below 2^-17 in magnitude are rounded to it, an
+ *      absolute change under 2^-25)
  *  - Layouts (row-major, innermost last):
  *      q, out       bf16  [B][T_max][Hq][D]
  *      k_pool       int8  [num_pages][Hkv][P][D]   (a page is P token rows)
- *      v_pool       int8  [num_pages][Hkv][D][P]   (a page is stored d-major)
+ *      v_pool       int8  [num_pages][Hkv][P/8][D][8]  (a page is two d-major
+ *                                  tiles of 8 tokens: token p, dim d at
+ *                                  ((p / 8) * D + d) * 8 + p % 8 in its page)
  *      k_scale,
  *      v_scale      fp16  [num_pages][Hkv][P]
  *      block_table  int32 [B][max_pages_per_seq]
