@@ -186,7 +186,8 @@ int splash_verify_attn_split_pages(int max_context_len, int P, int num_splits);
  *     out[b][t][h][:] = bf16( sum_s w_s part_o[b][h][t][s][:] / sum_s w_s )
  * summed in a fixed order that depends only on S (the result is
  * deterministic: the same inputs give the same bits); splits with lse = -inf
- * weigh nothing and their rows are not read.  part_o fp32 [B][Hq][T_max][S][D], part_lse fp32
+ * weigh nothing: their rows may be read (they must lie inside part_o) but
+ * never reach the result, whatever they hold.  part_o fp32 [B][Hq][T_max][S][D], part_lse fp32
  * [B][Hq][T_max][S].  Rows t >= draft_lens[b] of out are left untouched.
  */
 int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse,

@@ -38,6 +38,12 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
 // Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
 // gfx950 lane-swap instructions.  Swapping a register with itself exchanges the
 // odd 16-lane rows of one copy with the even rows of the other, so the two

@@ -510,19 +510,28 @@ __global__ __launch_bounds__(kWaves * 64) void verify_partition_kernel(const Ver
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of S context splits.  One workgroup (4 waves) per output
-// row: wave w accumulates splits s = w, w + 4, ... (eight loads in flight per
-// lane), then the four partial sums are added in wave order -- a fixed order,
-// so the result is deterministic.
+// Log-sum-exp merge of S context splits.  One workgroup per output row.  The
+// row's D columns are read as 16-byte groups; the 256 threads are NG groups of
+// D/4 threads, and group sg takes splits sg, sg + NG, ...  Every load of a
+// round (partial rows and log-sum-exps) is issued before any is used, so a
+// round costs one memory latency; S <= NG * kMergeUnroll takes one round.
+// M = max_s lse_s and W = sum_s e^(lse_s - M) are computed by every wave in the
+// same order; the groups' sums are added in group order.  Fixed orders
+// throughout, so the result is deterministic.  A split whose lse is -inf gets
+// weight 0 through a select, so its row (which may hold anything) never
+// reaches the sum.
 // ---------------------------------------------------------------------------
-constexpr int kMergeWaves = 4;
-constexpr int kMergeUnroll = 8;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeUnroll = 16;
 
 template <int D>
-__global__ __launch_bounds__(256) void splitk_merge_kernel(const MergeArgs a) {
-    constexpr int E = D / 64;
-    __shared__ float part[kMergeWaves - 1][D];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(const MergeArgs a) {
+    constexpr int C4 = D / 4;                                 // 16-byte column groups
+    constexpr int NG = kMergeThreads / C4;                    // split groups
+    constexpr float kLog2e = 1.4426950408889634f;
+    __shared__ f32x4_t red[NG][C4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c4 = tid % C4, sg = tid / C4;
     const int h = blockIdx.x % a.Hq;
     const int bt = blockIdx.x / a.Hq;
     const int t = bt % a.T_max;
@@ -531,58 +540,54 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(const MergeArgs a) {
     const int S = a.num_splits;
     const size_t prow = (((size_t)b * a.Hq + h) * a.T_max + t) * S;
     const float* lse = a.part_lse + prow;
-    float M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, lse[s]);
-    M = wave_max(M);                                          // identical in every wave
-    float W = 0.0f;                                           // identical in every lane: same order
-    for (int s = 0; s < S; ++s) {
-        const float l = lse[s];
-        if (l != -INFINITY) W += expf(l - M);
-    }
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    const float* src = a.part_o + prow * D + lane * E;
-    for (int s0 = wave; s0 < S; s0 += kMergeWaves * kMergeUnroll) {
-        float v[kMergeUnroll][E];
-        float w[kMergeUnroll];
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part_o + prow * D) + c4;
+
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float M = -INFINITY, W = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += NG * kMergeUnroll) {
+        f32x4_t v[kMergeUnroll];
+        float l[kMergeUnroll];
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const int s = s0 + u * kMergeWaves;
-            const float l = s < S ? lse[s] : -INFINITY;
-            w[u] = l == -INFINITY ? 0.0f : expf(l - M);
-            if (w[u] != 0.0f) {                               // an empty split's row is never read
-                if constexpr (E == 4) {
-                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + (size_t)s * D);
+            const int s = s0 + sg + u * NG;
+            v[u] = s < S ? src[(size_t)s * C4] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[u][e] = x[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) v[u][e] = src[(size_t)s * D + e];
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int s = s0 + sg + u * NG;
+            l[u] = s < S ? lse[s] : -INFINITY;
+        }
+        if (s0 == 0) {                                        // M and W over all splits, per wave
+            float mx = -INFINITY;
+            for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lse[s]);
+            M = wave_max(mx);
+            float ws = 0.0f;
+            if (M != -INFINITY)
+                for (int s = lane; s < S; s += 64) {
+                    const float x = lse[s];
+                    ws += x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) v[u][e] = 0.0f;
-            }
+            W = wave_sum(ws);
         }
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u)
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const bool live = l[u] != -INFINITY;
+            const float w = live ? __builtin_amdgcn_exp2f((l[u] - M) * kLog2e) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] += w[u] * v[u][e];
+            for (int e = 0; e < 4; ++e) acc[e] += live ? w * v[u][e] : 0.0f;
+        }
     }
-    if (wave > 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) part[wave - 1][lane * E + e] = acc[e];
-    }
+    red[sg][c4] = acc;
     __syncthreads();
-    if (wave == 0) {
+    if (sg == 0) {
+        f32x4_t x = red[0][c4];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float x = acc[e];
-#pragma unroll
-            for (int w2 = 0; w2 < kMergeWaves - 1; ++w2) x += part[w2][lane * E + e];
-            a.out[(((size_t)b * a.T_max + t) * a.Hq + h) * D + lane * E + e] = f32_to_bf16_rne(x / W);
-        }
+        for (int g2 = 1; g2 < NG; ++g2) x += red[g2][c4];
+        const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+        u32x2_t o;
+        o[0] = (uint32_t)f32_to_bf16_rne(x[0] * inv) | ((uint32_t)f32_to_bf16_rne(x[1] * inv) << 16);
+        o[1] = (uint32_t)f32_to_bf16_rne(x[2] * inv) | ((uint32_t)f32_to_bf16_rne(x[3] * inv) << 16);
+        *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.T_max + t) * a.Hq + h) * D + 4 * c4) = o;
     }
 }
 
@@ -613,9 +618,9 @@ hipError_t launch_splitk_merge(const MergeArgs& a, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     switch (a.D) {
-        case 64: hipLaunchKernelGGL((splitk_merge_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((splitk_merge_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, stream, a); break;
-        case 256: hipLaunchKernelGGL((splitk_merge_kernel<256>), dim3((unsigned)blocks), dim3(256), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((splitk_merge_kernel<64>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((splitk_merge_kernel<128>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a); break;
+        case 256: hipLaunchKernelGGL((splitk_merge_kernel<256>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
