@@ -148,7 +148,8 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
     const int L = pages_per_split(max_context_len, P, num_splits);
     const int S = ceil_div(ceil_div(max_context_len, P), L);     // splits that hold pages
     VerifyArgs a{q, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, block_table,
-                 max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale, S, L};
+                 max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale, S, L,
+                 num_pages};
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (S == 1) {
         a.out = out;
@@ -183,7 +184,7 @@ int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const 
     const int L = pages_per_split(max_context_len, P, num_splits);
     VerifyArgs a{q, nullptr, part_o, part_lse, k_pool, v_pool, k_scale, v_scale, block_table,
                  max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale,
-                 num_splits, L};
+                 num_splits, L, num_pages};
     return launch_verify_partition(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
                                                                                      : SPLASH_ERR_LAUNCH;
 }

@@ -40,6 +40,7 @@ struct VerifyArgs {
     float sm_scale;
     int num_splits;            // grid size along the context (S used in the layouts)
     int pages_per_split;       // L, a multiple of kPagesPerIter
+    int num_pages;             // pool size; page ids are clamped into [0, num_pages)
 };
 
 struct MergeArgs {

@@ -8,34 +8,39 @@
 // every page across the query heads of its group and all verify tokens (same
 // summary, section "Metal kernels generated to shape"; bnskd.com, "Tech core 2").
 //
-// Work decomposition.  One workgroup of 8 waves (two per SIMD, so that each
-// SIMD always has a second wave to issue from) per (request b, kv head g,
-// context split s).  Its rows are the R = G * d query rows that share kv head
-// g, ordered r = t * G + hh so that a shorter draft truncates a prefix of rows,
-// padded to tiles of 16; the tile count in use is a compile-time parameter of
-// the body.  The 8 waves are two row halves (half h owns tiles h, h+2, h+4)
-// times four: wave (h, w) computes scores for page w of each step and owns
-// head-dim quarter w of the output, for the rows of half h.
-//  * Q is loaded once, converted bf16 -> fp16 (exact for 2^-17 <= |q| <= 65504)
-//    and kept in registers as the B operand of 16x16x32 fp16 MFMAs.
+// Work decomposition.  One workgroup of four waves (one per SIMD) per
+// (request b, kv head g, context split s).  Its rows are the R = G * d query
+// rows that share kv head g, ordered r = t * G + hh so that a shorter draft
+// truncates a prefix of rows, padded to tiles of 16; the tile count in use is a
+// compile-time parameter of the body.  Every wave holds the queries of ALL rows
+// in registers, so each page is converted from int8 exactly once per workgroup:
 //  * The context is walked in steps of kPagesPerIter = 4 pages (64 tokens).
-//    Pages are copied HBM -> LDS with 16-byte direct-to-LDS loads into a ring
-//    of kStages steps, two steps ahead of their use; half 0 copies the K pages
-//    and the scales, half 1 the V pages.  K rows are XOR-swizzled by 16-byte
-//    chunk through the per-lane source address, which keeps the MFMA operand
-//    reads free of bank conflicts; V pages are stored as two d-major tiles of 8
-//    tokens, which gives the same property with a verbatim copy.
+//    Wave w owns page w of every step: it copies that page's K rows, scales and
+//    V rows HBM -> LDS with 16-byte direct-to-LDS loads, and computes the
+//    scores of all rows against its 16 keys.  For P V the waves split the head
+//    dimension instead (wave w owns columns [w * D/4, (w + 1) * D/4)).
+//  * Copies run three steps ahead: at step i a wave issues K(i + 3) and V(i + 1)
+//    (V is consumed two steps after K).  Rings of four K and four V steps hold
+//    them.  The page ids themselves travel through a small LDS ring, copied six
+//    steps ahead, so no copy waits on a block-table read.  Waits are explicit
+//    per-wave `s_waitcnt vmcnt(n)` with n the exact number of copies issued
+//    since; workgroup barriers wait only on LDS traffic.
+//  * One barrier per step.  Between two barriers a wave runs, for three steps
+//    at once: Q K^T of step i, the softmax of step i - 1 (whose row maxima were
+//    exchanged through the barrier) and P V of step i - 2 (whose P' tiles were).
 //  * int8 codes x become fp16 with one byte permute: binary16 0x64uu is
 //    1024 + u, and u = x + 128, so the operand holds 1152 + x exactly.  For K the
 //    bias is removed per row after the MFMA (sum_d q_d (1152 + x_d) - 1152 *
-//    sum_d q_d); for V it is subtracted exactly with a packed fp16 add.
-//  * Per step: S^T = K Q^T for the wave's page; scaled scores (K scale and
-//    softmax scale in log2 units, fp32); row maxima exchanged in LDS among the
-//    half's four waves; p = exp2(z - m) against a lazily moved reference m;
-//    P' = p * s_v written as fp16 to LDS; then O^T += V^T P'^T for the wave's
-//    head-dim quarter over the step's 64 keys.  The P V product of a step runs
-//    after the next step's Q K^T, inside the same barrier interval, so each
-//    step needs two workgroup barriers.
+//    sum_d q_d, the second sum also taken on the MFMA); for V it is subtracted
+//    exactly with a packed fp16 add before the MFMA.
+//  * Scores are kept relative to a per-row reference m that moves lazily: only
+//    when a step's maximum exceeds it by more than tau (log2 units, 8 unless a
+//    V scale of the step exceeds 255, then 0), so p = exp2(z - m) <= 2^tau and
+//    P' = p * s_v stays inside fp16.  The O and row-sum rescale is skipped by
+//    ballot when no row moved.
+//  * Q K^T uses v_mfma_f32_16x16x32_f16 (S^T = K Q^T, one 16-key page x 16 rows
+//    per tile); P V uses v_mfma_f32_32x32x16_f16 (O^T = V^T P'^T, 32 columns x
+//    32 rows x one page of keys).
 //  * The epilogue divides by the row sums and writes bf16 rows (one split) or
 //    fp32 partial rows plus their natural-log log-sum-exp (several splits).
 #include <math.h>
@@ -45,9 +50,13 @@
 
 namespace splash {
 
-constexpr int kStages = 4;     // LDS ring of page steps (two ahead, one in Q K^T, one in P V)
-constexpr int kWaves = 8;      // two row halves x four
+constexpr int kWaves = 8;      // two waves per SIMD
+constexpr int kRing = 4;       // K and V rings, in steps
+constexpr int kKAhead = 3;     // K(i + 3) is issued at step i
+constexpr int kIdAhead = 7;    // the page id of step i + 7 is copied at step i
+constexpr int kIdRing = 8;
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // 32-bit LDS address of a pointer into the workgroup's LDS.
@@ -58,7 +67,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Direct-to-LDS loads: lane i's 16 (or 4) bytes land at LDS address
 // m0 + 16 * i (4 * i).  Issued as inline assembly so that the compiler adds no
 // wait of its own: these copies are waited for explicitly (wait_vmcnt) before
-// the barrier that publishes a stage.  `lds` must be uniform in the wave.
+// the barrier that publishes them.  `lds` must be uniform in the wave.
 // Ordering: volatile asm statements keep their order, and the barrier and
 // wait statements carry the memory clobber that orders the LDS reads.
 __device__ __forceinline__ void dma16_to_lds(const void* src, uint32_t lds) {
@@ -68,18 +77,28 @@ __device__ __forceinline__ void dma4_to_lds(const void* src, uint32_t lds) {
     asm volatile("global_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds));
 }
 
-// Block-table entry through the scalar cache (the table is read-only here).
-// As a plain C++ load the compiler would use a vector load whose wait also
-// drains the in-flight page copies.
-__device__ __forceinline__ int load_page_id(const int32_t* p) {
-    int v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-    return v;
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most c of this wave's vector-memory loads are outstanding
+// (c is wave-uniform).  Counts above the table wait for all.
+__device__ __forceinline__ void wait_vmcnt_le(int c) {
+    switch (c) {
+#define SPLASH_VMCNT_CASE(N) \
+    case N: wait_vmcnt<N>(); break;
+        SPLASH_VMCNT_CASE(0) SPLASH_VMCNT_CASE(1) SPLASH_VMCNT_CASE(2) SPLASH_VMCNT_CASE(3)
+        SPLASH_VMCNT_CASE(4) SPLASH_VMCNT_CASE(5) SPLASH_VMCNT_CASE(6) SPLASH_VMCNT_CASE(7)
+        SPLASH_VMCNT_CASE(8) SPLASH_VMCNT_CASE(9) SPLASH_VMCNT_CASE(10) SPLASH_VMCNT_CASE(11)
+        SPLASH_VMCNT_CASE(12) SPLASH_VMCNT_CASE(13) SPLASH_VMCNT_CASE(14) SPLASH_VMCNT_CASE(15)
+        SPLASH_VMCNT_CASE(16) SPLASH_VMCNT_CASE(17) SPLASH_VMCNT_CASE(18) SPLASH_VMCNT_CASE(19)
+        SPLASH_VMCNT_CASE(20) SPLASH_VMCNT_CASE(21) SPLASH_VMCNT_CASE(22) SPLASH_VMCNT_CASE(23)
+        SPLASH_VMCNT_CASE(24) SPLASH_VMCNT_CASE(25) SPLASH_VMCNT_CASE(26) SPLASH_VMCNT_CASE(27)
+        SPLASH_VMCNT_CASE(28) SPLASH_VMCNT_CASE(29) SPLASH_VMCNT_CASE(30) SPLASH_VMCNT_CASE(31)
+#undef SPLASH_VMCNT_CASE
+        default: wait_vmcnt<0>(); break;
+    }
 }
 
 // Workgroup barrier for LDS traffic only: outstanding direct-to-LDS copies stay
@@ -88,18 +107,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Codes 0-1 (sel 0) or 2-3 (sel 1) of a dword -> two fp16 values 1152 + code.
-__device__ __forceinline__ uint32_t codes2_to_f16_biased(uint32_t raw, int sel) {
-    const uint32_t u = raw ^ 0x80808080u;
+// Codes 0-1 (sel 0) or 2-3 (sel 1) of a dword already XORed with 0x80808080
+// -> two fp16 values 1152 + code.
+__device__ __forceinline__ uint32_t ucodes2_to_f16(uint32_t u, int sel) {
     return __builtin_amdgcn_perm(0x64646464u, u, sel ? 0x04030402u : 0x04010400u);
 }
 
 // 16 codes -> two fp16x8 operands holding 1152 + code.
 __device__ __forceinline__ void codes16_to_f16_biased(const u32x4_t raw, f16x8_t& lo, f16x8_t& hi) {
-    const u32x4_t a = {codes2_to_f16_biased(raw[0], 0), codes2_to_f16_biased(raw[0], 1),
-                       codes2_to_f16_biased(raw[1], 0), codes2_to_f16_biased(raw[1], 1)};
-    const u32x4_t b = {codes2_to_f16_biased(raw[2], 0), codes2_to_f16_biased(raw[2], 1),
-                       codes2_to_f16_biased(raw[3], 0), codes2_to_f16_biased(raw[3], 1)};
+    u32x4_t a, b;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t u0 = raw[k] ^ 0x80808080u, u1 = raw[2 + k] ^ 0x80808080u;
+        a[2 * k] = ucodes2_to_f16(u0, 0);
+        a[2 * k + 1] = ucodes2_to_f16(u0, 1);
+        b[2 * k] = ucodes2_to_f16(u1, 0);
+        b[2 * k + 1] = ucodes2_to_f16(u1, 1);
+    }
     lo = bit_cast<f16x8_t>(a);
     hi = bit_cast<f16x8_t>(b);
 }
@@ -109,360 +133,726 @@ __device__ __forceinline__ f16x8_t codes8_to_f16(const u32x2_t raw) {
     const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
     u32x4_t h;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        h[k] = bit_cast<uint32_t>(bit_cast<f16x2_t>(codes2_to_f16_biased(raw[k >> 1], k & 1)) - bias);
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t u = raw[k] ^ 0x80808080u;
+        h[2 * k] = bit_cast<uint32_t>(bit_cast<f16x2_t>(ucodes2_to_f16(u, 0)) - bias);
+        h[2 * k + 1] = bit_cast<uint32_t>(bit_cast<f16x2_t>(ucodes2_to_f16(u, 1)) - bias);
+    }
     return bit_cast<f16x8_t>(h);
 }
 
-__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) { return (float)bit_cast<_Float16>((uint16_t)b); }
+__device__ __forceinline__ float f16lo(uint32_t b) { return (float)bit_cast<_Float16>((uint16_t)b); }
+__device__ __forceinline__ float f16hi(uint32_t b) { return (float)bit_cast<_Float16>((uint16_t)(b >> 16)); }
 
-// LDS arena of one workgroup.
+// fp32 pair -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
+    const f16x2_t h = {(_Float16)x, (_Float16)y};
+    return bit_cast<uint32_t>(h);
+}
+
+// Q K^T MFMAs (v_mfma_f32_16x16x32_f16) with the query operands read straight
+// from AGPRs, where the queries of all rows stay resident.  Written as inline
+// assembly because the compiler's MFMA selection here reads both sources from
+// VGPRs and would copy every query operand back per instruction.  The wait
+// states the compiler would insert around these MFMAs are written out: two
+// before a block (a VALU write of a source operand just before), none between
+// accumulations into the same registers, and qk_drain() after the last block,
+// before any VALU reads an accumulator (the MFMA result latency).
+// One K chunk of Q K^T for NT row tiles: the K-operand pair (k0, k1) against the
+// query operands of every tile, k0 for all tiles first, then k1, so that
+// accumulations into one tile are NT instructions apart.  FIRST starts the
+// accumulators from zero.  One leading s_nop covers a VALU write of k0/k1 just
+// before the block.
+template <int NT, bool FIRST>
+__device__ __forceinline__ void qk_chunk(f32x4_t* acc, const f16x8_t k0, const f16x8_t k1, const f16x8_t* q0,
+                                         const f16x8_t* q1) {
+    static_assert(NT >= 1 && NT <= 8, "tile count");
+    if constexpr (NT == 1 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %1, %3, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %2, %4, %0"
+            : "=&v"(acc[0])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q1[0]));
+    if constexpr (NT == 1 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %1, %3, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %2, %4, %0"
+            : "+v"(acc[0])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q1[0]));
+    if constexpr (NT == 2 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %2, %4, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %2, %5, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %3, %6, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %3, %7, %1"
+            : "=&v"(acc[0]), "=&v"(acc[1])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q1[0]), "a"(q1[1]));
+    if constexpr (NT == 2 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %2, %4, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %2, %5, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %3, %6, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %3, %7, %1"
+            : "+v"(acc[0]), "+v"(acc[1])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q1[0]), "a"(q1[1]));
+    if constexpr (NT == 3 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %3, %5, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %3, %6, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %3, %7, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %4, %8, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %4, %9, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %4, %10, %2"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]));
+    if constexpr (NT == 3 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %3, %5, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %3, %6, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %3, %7, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %4, %8, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %4, %9, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %4, %10, %2"
+            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]));
+    if constexpr (NT == 4 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %4, %6, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %4, %7, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %4, %8, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %4, %9, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %5, %10, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %5, %11, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %5, %12, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %5, %13, %3"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]));
+    if constexpr (NT == 4 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %4, %6, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %4, %7, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %4, %8, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %4, %9, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %5, %10, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %5, %11, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %5, %12, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %5, %13, %3"
+            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]));
+    if constexpr (NT == 5 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %5, %7, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %5, %8, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %5, %9, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %5, %10, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %5, %11, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %6, %12, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %6, %13, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %6, %14, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %6, %15, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %6, %16, %4"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]));
+    if constexpr (NT == 5 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %5, %7, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %5, %8, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %5, %9, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %5, %10, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %5, %11, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %6, %12, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %6, %13, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %6, %14, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %6, %15, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %6, %16, %4"
+            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]));
+    if constexpr (NT == 6 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %6, %8, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %6, %9, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %6, %10, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %6, %11, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %6, %12, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %6, %13, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %7, %14, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %7, %15, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %7, %16, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %7, %17, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %7, %18, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %7, %19, %5"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]));
+    if constexpr (NT == 6 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %6, %8, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %6, %9, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %6, %10, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %6, %11, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %6, %12, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %6, %13, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %7, %14, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %7, %15, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %7, %16, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %7, %17, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %7, %18, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %7, %19, %5"
+            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]));
+    if constexpr (NT == 7 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %7, %9, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %7, %10, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %7, %11, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %7, %12, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %7, %13, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %7, %14, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %7, %15, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %8, %16, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %8, %17, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %8, %18, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %8, %19, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %8, %20, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %8, %21, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %8, %22, %6"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5]), "=&v"(acc[6])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]));
+    if constexpr (NT == 7 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %7, %9, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %7, %10, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %7, %11, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %7, %12, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %7, %13, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %7, %14, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %7, %15, %6\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %8, %16, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %8, %17, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %8, %18, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %8, %19, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %8, %20, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %8, %21, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %8, %22, %6"
+            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]));
+    if constexpr (NT == 8 && FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %8, %10, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %8, %11, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %8, %12, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %8, %13, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %8, %14, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %8, %15, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %8, %16, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %7, %8, %17, 0\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %9, %18, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %9, %19, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %9, %20, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %9, %21, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %9, %22, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %9, %23, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %9, %24, %6\n\t"
+            "v_mfma_f32_16x16x32_f16 %7, %9, %25, %7"
+            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5]), "=&v"(acc[6]), "=&v"(acc[7])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q0[7]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]), "a"(q1[7]));
+    if constexpr (NT == 8 && !FIRST)
+        asm("s_nop 1\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %8, %10, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %8, %11, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %8, %12, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %8, %13, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %8, %14, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %8, %15, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %8, %16, %6\n\t"
+            "v_mfma_f32_16x16x32_f16 %7, %8, %17, %7\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %9, %18, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %9, %19, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %9, %20, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %9, %21, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %9, %22, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %9, %23, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %9, %24, %6\n\t"
+            "v_mfma_f32_16x16x32_f16 %7, %9, %25, %7"
+            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7])
+            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q0[7]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]), "a"(q1[7]));
+}
+
+// Result latency of the last Q K^T MFMAs before VALU reads: 13 wait states (the
+// compiler uses 8 for this instruction).  Every accumulator passes through the
+// statement, so no read of one can be scheduled above it.
+template <int N>
+__device__ __forceinline__ void qk_drain(f32x4_t* acc) {
+#define SPLASH_DRAIN "s_nop 7\n\ts_nop 4"
+    static_assert(N >= 1 && N <= 8, "tile count");
+    if constexpr (N == 1) asm(SPLASH_DRAIN : "+v"(acc[0]));
+    if constexpr (N == 2) asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]));
+    if constexpr (N == 3) asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]));
+    if constexpr (N == 4) asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+    if constexpr (N == 5)
+        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]));
+    if constexpr (N == 6)
+        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]));
+    if constexpr (N == 7)
+        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+            "+v"(acc[6]));
+    if constexpr (N == 8)
+        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+            "+v"(acc[6]), "+v"(acc[7]));
+#undef SPLASH_DRAIN
+}
+
+// Shapes and the LDS arena of one workgroup.
 template <int D, int G>
-struct Arena {
-    static constexpr int PAGE = kPage * D;                    // bytes of one K or V page (one kv head)
-    static constexpr int SCALES = 2 * kPage * 2;              // 16 fp16 K scales then 16 fp16 V scales
-    static constexpr int STAGE = kPagesPerIter * (2 * PAGE + SCALES);
-    static constexpr int k_off(int j) { return j * PAGE; }
-    static constexpr int v_off(int j) { return kPagesPerIter * PAGE + j * PAGE; }
-    static constexpr int s_off(int j) { return 2 * kPagesPerIter * PAGE + j * SCALES; }
-    static constexpr int NT = G;                              // row tiles for up to 16 drafts
-    static constexpr int NTH = (NT + 1) / 2;                  // row tiles per half
-    static constexpr int P_OFF = kStages * STAGE;             // two buffers of P'^T operand tiles, fp16
-    static constexpr int P_BUF = 2 * (kPagesPerIter / 2) * NTH * 64 * 16;   // [half][kb2][tile][lane][16 B]
-    static constexpr int RED_OFF = P_OFF + 2 * P_BUF;         // [row][page] fp32 maxima / sums,
-    static constexpr int TOTAL = RED_OFF + (NT * 16 + 1) * 4 * 4;   // then [page] V-scale maxima
+struct Cfg {
+    static constexpr int NT = G;                      // 16-row tiles at 16 drafts
+    static constexpr int KB = D / 32;                 // contraction blocks of Q K^T
+    static constexpr int CH = D / 16;                 // 16-byte chunks of a K row
+    static constexpr int QCH = D / 8;                 // 16-byte chunks of a Q row (bf16, then fp16)
+    static constexpr int QSWZ = QCH < 16 ? QCH : 16;  // Q rows are XOR-swizzled over this many chunks
+    static constexpr int PAGE = kPage * D;            // bytes of one K or V page (one kv head)
+    static constexpr int NI = PAGE / 1024;            // 16-byte copies per lane per page
+    static constexpr int PVW = D / 32 < kWaves ? D / 32 : kWaves;   // waves taking part in P V, 32 columns each
+    static constexpr int NT32 = (NT + 1) / 2;         // 32-row tiles at 16 drafts
+    static constexpr int SLOT = kPagesPerIter * PAGE; // one step of K (or V) pages
+    static constexpr int SSLOT = kPagesPerIter * 64;  // one step of scales: per page 16 K then 16 V (fp16)
+    static constexpr int K_OFF = 0;
+    static constexpr int S_OFF = K_OFF + kRing * SLOT;
+    static constexpr int ID_OFF = S_OFF + kRing * SSLOT;            // page ids [kIdRing][page] int32
+    static constexpr int F_OFF = ID_OFF + kIdRing * kPagesPerIter * 4;   // two buffers of [wave] step flags
+    static constexpr int V_OFF = F_OFF + 2 * kWaves * 4;
+    static constexpr int P_OFF = V_OFF + kRing * SLOT;              // two buffers of P'^T operands
+    static constexpr int PBUF = kPagesPerIter * NT32 * 64 * 16;     // [page][32-row tile][lane][16 B]
+    static constexpr int M_OFF = P_OFF + 2 * PBUF;                  // [row][page] maxima or row sums
+    static constexpr int R_OFF = M_OFF + NT * 16 * kPagesPerIter * 4;   // [row] O rescale factors / references
+    static constexpr int TOTAL = R_OFF + NT * 16 * 4;
+    static constexpr int Q_OFF = V_OFF + SLOT;        // start-up only: Q over the V slots 1.. onwards
+    static constexpr int QBYTES = NT * 16 * D * 2;
+    static_assert(D % 64 == 0 && PVW >= 1, "head dim must be a multiple of 64");
+    static_assert(NT % 2 == 0, "the two row halves hold whole tiles");
+    static_assert(PAGE % 1024 == 0, "page must be whole 1 KB copies");
+    static_assert(Q_OFF + QBYTES <= TOTAL, "Q staging does not fit");
     static_assert(TOTAL <= 160 * 1024, "LDS arena exceeds 160 KB");
 };
 
-template <int D>
-struct Tiles {
-    static constexpr int KB = D / 32;         // contraction blocks of Q K^T
-    static constexpr int CH = D / 16;         // 16-byte chunks in a K row
-    static constexpr int DW = D / 4;          // head-dim columns each wave owns in P V
-    static constexpr int MT = DW / 16;        // V^T tiles of 16 columns per wave
-    static constexpr int NI = kPage * D / 1024;   // 16-byte copies per lane per page
-    static constexpr int SWZ_DIV = CH >= 8 ? 1 : 8 / CH;
-    static constexpr int SWZ_MOD = CH >= 8 ? 8 : CH;
-    static_assert(D % 64 == 0 && MT >= 1, "head dim must be a multiple of 64");
-};
-
-// XOR swizzle of 16-byte chunks inside a K row, by slot.
+// XOR swizzle of 16-byte chunks inside a K row, by slot: the 16 lanes reading
+// one chunk column of 16 different rows hit different banks.
 template <int D>
 __device__ __forceinline__ int k_swizzle(int slot) {
-    return (slot / Tiles<D>::SWZ_DIV) % Tiles<D>::SWZ_MOD;
+    constexpr int CH = D / 16;
+    return CH >= 8 ? (slot & 7) : ((slot / (8 / CH)) % CH);
 }
 
-// Half 0 wave w copies the K page and the scales of page w of a step into the
-// stage at LDS address `stage`; half 1 wave w copies its V page.
-template <int D, int G>
-__device__ __forceinline__ void stage_page(uint32_t stage, int half, int w, int lane, const VerifyArgs& a,
-                                           int page, int g) {
-    using A = Arena<D, G>;
-    using T = Tiles<D>;
-    const size_t blk = (size_t)page * a.Hkv + g;
-    if (half == 0) {
-        const int8_t* kp = a.k_pool + blk * A::PAGE;
-#pragma unroll
-        for (int i = 0; i < T::NI; ++i) {
-            const int c = 64 * i + lane;                      // LDS chunk of this lane
-            const int slot = c / T::CH, pc = c % T::CH;
-            const int lc = pc ^ k_swizzle<D>(slot);           // logical chunk stored there
-            dma16_to_lds(kp + slot * D + 16 * lc, stage + A::k_off(w) + 1024 * i);
-        }
-        if (lane < 16) {
-            const uint16_t* src = lane < 8 ? a.k_scale + blk * kPage + 2 * lane
-                                           : a.v_scale + blk * kPage + 2 * (lane - 8);
-            dma4_to_lds(src, stage + A::s_off(w));
-        }
-    } else {
-        const int8_t* vp = a.v_pool + blk * A::PAGE;
-#pragma unroll
-        for (int i = 0; i < T::NI; ++i) dma16_to_lds(vp + 1024 * i + 16 * lane, stage + A::v_off(w) + 1024 * i);
-    }
+// 16 bytes of LDS straight into an AGPR quad.  The compiler does not track this
+// load: it is followed by an explicit s_waitcnt lgkmcnt(0) before any use.
+__device__ __forceinline__ f16x8_t lds_read_agpr(uint32_t addr) {
+    f16x8_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=a"(v) : "v"(addr));
+    return v;
 }
 
+// The body for NTU row tiles in use.  Wave v = 4 h + w: row half h holds tiles
+// [h NH, (h + 1) NH) (NH = ceil(NTU / 2); a tile past NTU is padding with
+// q = 0) and takes page w of every step for Q K^T and the softmax; half 0 copies
+// the K pages, their scales and the page ids, half 1 the V pages.  For P V the
+// waves split the head dimension: wave v owns columns [32 v, 32 v + 32) of all
+// rows, so every V code is converted once.
 template <int D, int G, int NTU>
 __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds, const int b, const int g,
                                                const int s, const int dl, const int ctx, const int pg_begin,
                                                const int pg_end) {
-    using A = Arena<D, G>;
-    using T = Tiles<D>;
-    constexpr int KB = T::KB, DW = T::DW, MT = T::MT;
-    constexpr int NTH = (NTU + 1) / 2;                        // tiles of this body per half
-    constexpr int LOADS_H0 = T::NI + 1, LOADS_H1 = T::NI;     // copies per wave per step
+    using C = Cfg<D, G>;
+    constexpr int KB = C::KB, NI = C::NI;
+    constexpr int NH = (NTU + 1) / 2;                         // 16-row tiles per half
+    constexpr int NT32 = NH;                                  // 32-row tiles in use (P V)
+    constexpr int QCHUNKS = 2 * NH * 16 * C::QCH;             // 16-byte chunks of Q converted (padding included)
+    constexpr int QI = (QCHUNKS + 64 * kWaves - 1) / (64 * kWaves);   // Q chunks per lane
+    constexpr int STEADY_K = 2 * (NI + 2);                    // copies of a K wave in two steady steps
+    constexpr int STEADY_V = 2 * NI;                          // of a V wave
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kLn2 = 0.6931471805599453f;
+    constexpr float kTau = 8.0f;                              // lazy-reference slack, log2 units
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = wave >> 2, w = wave & 3;
+    const int v = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = v >> 2, w = v & 3;
     const int gq = lane >> 4, li = lane & 15;
     const int rows = G * dl;
     const int Hq = a.Hq, S = a.num_splits;
-    const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq;
-    const int n_steps = (pg_end - pg_begin + kPagesPerIter - 1) / kPagesPerIter;
-    // half 1 has one tile fewer when the tile count is odd
-    const bool last_tile = (half == 0) || (NTU % 2 == 0);
+    const int n = (pg_end - pg_begin + kPagesPerIter - 1) / kPagesPerIter;   // steps
+    const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq + pg_begin + w;   // + 4 j
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    const int last_valid = (pg_end - pg_begin - 1 - w) >> 2;  // last step with a page w
+    const int t0 = h * NH;                                    // first tile of this half
 
-    auto issue_step = [&](int step) {
-        int pg = pg_begin + step * kPagesPerIter + w;
-        if (pg >= pg_end) pg = pg_end - 1;                    // past the split: copy a valid page, masked later
-        stage_page<D, G>(lds_base + (step % kStages) * A::STAGE, half, w, lane, a, load_page_id(bt + pg), g);
+    // copies this wave issues at pipeline position k (k = -3, -2, -1 are the start-up)
+    auto count_at = [&](int k) -> int {
+        int c = 0;
+        if (h == 0) {
+            if (k + kKAhead >= 0 && k + kKAhead <= last_valid) c += NI + 1;
+            if (k >= 0 && k + kIdAhead <= last_valid) c += 1;
+        } else {
+            if (k + 1 >= 0 && k + 1 <= last_valid) c += NI;
+        }
+        return c;
     };
-    issue_step(0);
-    if (n_steps > 1) issue_step(1);
-
-    // ---- Q for this half's tiles (tile i of the half is row tile half + 2 i), fp16,
-    // as the B operand of S^T = K Q^T; the per-row code bias 1152 * sum_d q_d
-    f16x8_t qf[NTH][KB];
-    float qbias[NTH];
+    // per-lane byte offsets of the K copies inside a page (rows XOR-swizzled by chunk)
+    int koff[NI];
 #pragma unroll
-    for (int i = 0; i < NTH; ++i) {
-        const int row = (half + 2 * i) * 16 + li;
-        const bool ok = row < rows && (i + 1 < NTH || last_tile);
-        const int t = ok ? row / G : 0, h = g * G + (ok ? row % G : 0);
-        const uint16_t* qrow = a.q + (((size_t)b * a.T_max + t) * Hq + h) * D;
-        float acc = 0.0f;
+    for (int i = 0; i < NI; ++i) {
+        const int c = 64 * i + lane;
+        const int slot = c / C::CH, pc = c % C::CH;
+        koff[i] = h == 0 ? slot * D + 16 * (pc ^ k_swizzle<D>(slot)) : 1024 * i + 16 * lane;
+    }
+    const int soff = lane < 8 ? 2 * lane : 2 * (lane - 8);    // scale copy: lanes 0-7 K, 8-15 V
+    // K wave: page w's K rows and scales of step j; V wave: its V rows
+    auto issue = [&](int j, int page) {
+        const size_t blk = (size_t)page * a.Hkv + g;
+        const int8_t* src = (h == 0 ? a.k_pool : a.v_pool) + blk * C::PAGE;
+        const uint32_t dst = lds_base + (h == 0 ? C::K_OFF : C::V_OFF) + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma16_to_lds(src + koff[i], dst + 1024 * i);
+        if (h == 0 && lane < 16)
+            dma4_to_lds((lane < 8 ? a.k_scale : a.v_scale) + blk * kPage + soff,
+                        lds_base + C::S_OFF + (j & (kRing - 1)) * C::SSLOT + w * 64);
+    };
+    // page id of step j from the id ring, clamped into the pool so that no copy
+    // can leave it
+    auto ring_id = [&](int j) -> int {
+        return *reinterpret_cast<const int*>(lds + C::ID_OFF + ((j & (kIdRing - 1)) * kPagesPerIter + w) * 4);
+    };
+    auto clamp_page = [&](int x) -> int { return min(max(__builtin_amdgcn_readfirstlane(x), 0), a.num_pages - 1); };
+
+    // ---- start-up.  Page ids of steps 0..kIdAhead-1 (plain loads, waited here,
+    // before any copy is in flight), then Q into LDS, then the first copies.
+    int ids0 = 0;
+    if (lane < kIdAhead && lane <= last_valid) ids0 = bt[4 * lane];
+    if (h == 0 && lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + w) * 4) = ids0;
+#pragma unroll
+    for (int k = 0; k < QI; ++k) {
+        const int c = 64 * (v + kWaves * k) + lane;           // Q chunk this lane copies
+        const int row = c / C::QCH, pc = c % C::QCH;
+        if (row < rows) {
+            const int lc = pc ^ (row % C::QSWZ);
+            const int t = row / G, hq = g * G + row % G;
+            dma16_to_lds(a.q + (((size_t)b * a.T_max + t) * Hq + hq) * D + 8 * lc,
+                         lds_base + C::Q_OFF + 1024 * (v + kWaves * k));
+        }
+    }
+#pragma unroll
+    for (int k = -kKAhead; k < 0; ++k) {
+        if (h == 0 && k + kKAhead <= last_valid) issue(k + kKAhead, clamp_page(__builtin_amdgcn_readlane(ids0, k + kKAhead)));
+        if (h == 1 && k + 1 >= 0 && k + 1 <= last_valid) issue(k + 1, clamp_page(__builtin_amdgcn_readlane(ids0, k + 1)));
+    }
+    wait_vmcnt_le(count_at(-3) + count_at(-2) + count_at(-1));   // this lane's Q chunks have landed
+    // bf16 -> fp16 in place, each lane its own chunks (exact for 2^-17 <= |q| <= 65504);
+    // padded rows become q = 0.  All reads first, then all writes.
+    {
+        u32x4_t raw[QI];
+#pragma unroll
+        for (int k = 0; k < QI; ++k) {
+            const int c = 64 * (v + kWaves * k) + lane;
+            raw[k] = (QCHUNKS % (64 * kWaves) == 0 || c < QCHUNKS)
+                         ? *reinterpret_cast<const u32x4_t*>(lds + C::Q_OFF + 16 * c)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < QI; ++k) {
+            const int c = 64 * (v + kWaves * k) + lane;
+            const uint32_t okmask = c / C::QCH < rows ? 0xffffffffu : 0u;
+            u32x4_t hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = raw[k][e] & okmask;
+                hv[e] = pack_f16x2(bit_cast<float>(x << 16), bit_cast<float>(x & 0xffff0000u));
+            }
+            if (QCHUNKS % (64 * kWaves) == 0 || c < QCHUNKS)
+                *reinterpret_cast<u32x4_t*>(lds + C::Q_OFF + 16 * c) = hv;
+        }
+    }
+    lds_barrier();
+
+    // ---- this half's Q as fp16 B operands, resident in AGPRs, and the per-row
+    // K-code bias 1152 * sum_d q_d taken on the MFMA
+    f16x8_t qf[KB][NH];
+    float qb[NH];
+    {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const int d0 = 64 * (kb >> 1) + 16 * gq + 8 * (kb & 1);
-            u32x4_t raw = u32x4_t{0u, 0u, 0u, 0u};
-            if (ok) raw = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-            f16x8_t hv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = bit_cast<float>(e & 1 ? raw[e >> 1] & 0xffff0000u : raw[e >> 1] << 16);
-                hv[e] = (_Float16)f;
-                acc += (float)hv[e];
+            for (int i = 0; i < NH; ++i) {
+                const int row = 16 * (t0 + i) + li;
+                const int lc = 8 * (kb >> 1) + 2 * gq + (kb & 1);   // logical 16-byte chunk of d
+                qf[kb][i] = lds_read_agpr(lds_base + C::Q_OFF + row * (2 * D) + 16 * (lc ^ (row % C::QSWZ)));
             }
-            qf[i][kb] = hv;
         }
-        qbias[i] = group4_sum(acc) * 1152.0f;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the AGPR loads above
+        f16x8_t k1152;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k1152[e] = (_Float16)1152.0f;
+        f32x4_t acc[NH];
+        qk_chunk<NH, true>(acc, k1152, k1152, qf[0], qf[1]);
+#pragma unroll
+        for (int c = 1; c < KB / 2; ++c) qk_chunk<NH, false>(acc, k1152, k1152, qf[2 * c], qf[2 * c + 1]);
+        qk_drain<NH>(acc);
+#pragma unroll
+        for (int i = 0; i < NH; ++i) qb[i] = acc[i][0];
     }
 
-    float m_run[NTH], l_run[NTH];
-    f32x4_t o[MT][NTH];
+    // per-row state of this half's tiles (row 16 (t0 + i) + li, the same in all lanes of a row)
+    float m_ref[NH], nmr[NH], l_run[NH], thr[NH];
 #pragma unroll
-    for (int i = 0; i < NTH; ++i) {
-        m_run[i] = -INFINITY;
+    for (int i = 0; i < NH; ++i) {
+        m_ref[i] = -INFINITY;                                 // no key seen yet
+        nmr[i] = 0.0f;                                        // -(m_ref if finite, else 0)
         l_run[i] = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[mt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        thr[i] = -INFINITY;                                   // -inf until the row has a reference, then tau
     }
+    f32x16_t o[NT32];                                         // O^T, columns [32 v, 32 v + 32) of all rows
+#pragma unroll
+    for (int r = 0; r < NT32; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[r][e] = 0.0f;
+
+    f32x4_t zs[NH];                                           // scores of the previous step, relative to m
+    float vsc[4];                                             // V scales of the previous step's keys
+#pragma unroll
+    for (int i = 0; i < NH; ++i) zs[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vsc[j] = 0.0f;
     const float zscale = a.sm_scale * kLog2e;
-    float* red = reinterpret_cast<float*>(lds + A::RED_OFF);
-    // P' tiles of this half: [buf][half][kb2][tile][lane][8 fp16]
-    auto pbuf = [&](int buf, int kb2, int i) {
-        return reinterpret_cast<_Float16*>(lds + A::P_OFF + buf * A::P_BUF) +
-               (((half * (kPagesPerIter / 2) + kb2) * NTH + i) * 64) * 8;
-    };
+    float* const red = reinterpret_cast<float*>(lds + C::M_OFF);
+    float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
+    int id_next = h == 0 ? clamp_page(__builtin_amdgcn_readlane(ids0, kKAhead)) : clamp_page(__builtin_amdgcn_readlane(ids0, 1));
 
-    for (int it = 0; it <= n_steps; ++it) {
-        // stage `it` copied (this wave's part) and visible to all after the barrier;
-        // also publishes P'(it - 1)
-        if (it < n_steps) {
-            if (it + 1 < n_steps) {
-                if (half == 0) wait_vmcnt<LOADS_H0>(); else wait_vmcnt<LOADS_H1>();
-            } else {
-                wait_vmcnt<0>();
-            }
+    for (int it = 0; it < n + 2; ++it) {
+        // this wave's copies of K(it) or V(it - 2) have landed; the barrier
+        // publishes them, the flags of step it - 1 and the P' tiles of step it - 2
+        if (it >= 2 && it + kIdAhead - 1 <= last_valid) {
+            if (h == 0) wait_vmcnt<STEADY_K>(); else wait_vmcnt<STEADY_V>();
+        } else {
+            wait_vmcnt_le(count_at(it - 2) + count_at(it - 1));
         }
         lds_barrier();
-        if (it + 2 < n_steps) issue_step(it + 2);             // into the slot of step it - 2
+        const bool do_sm = it >= 1 && it <= n;
+        u32x4_t fl0 = u32x4_t{0u, 0u, 0u, 0u}, fl1 = fl0;
+        if (do_sm) {
+            fl0 = *reinterpret_cast<const u32x4_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves * 4);
+            fl1 = *reinterpret_cast<const u32x4_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves * 4 + 16);
+        }
+        // ---- copies for later steps
+        if (h == 0) {
+            if (it + kKAhead <= last_valid) issue(it + kKAhead, id_next);
+            if (it + kIdAhead <= last_valid && lane == 0)
+                dma4_to_lds(bt + 4 * (it + kIdAhead),
+                            lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + w) * 4);
+        } else {
+            if (it + 1 <= last_valid) issue(it + 1, id_next);
+        }
 
-        // ---- P V for the previous step: O^T += V^T P'^T (this wave's head-dim quarter)
-        if (it >= 1) {
-            const int pstep = it - 1;
-            const uint8_t* pst = lds + (pstep % kStages) * A::STAGE;
-            const int ppg0 = pg_begin + pstep * kPagesPerIter;
+        // ---- P V of step it - 2: O^T += V^T P'^T for this wave's 32 columns
+        if (it >= 2 && v < C::PVW) {
+            const int pstep = it - 2;
+            const int npages = min(kPagesPerIter, pg_end - pg_begin - kPagesPerIter * pstep);
+            const uint8_t* vst = lds + C::V_OFF + (pstep & (kRing - 1)) * C::SLOT + (lane >> 5) * (D * 8) +
+                                 (32 * v + (lane & 31)) * 8;
+            const uint8_t* pbr = lds + C::P_OFF + (pstep & 1) * C::PBUF + lane * 16;
 #pragma unroll
-            for (int kb2 = 0; kb2 < kPagesPerIter / 2; ++kb2) {
-                if (ppg0 + 2 * kb2 < pg_end) {                // uniform
-                    f16x8_t pf[NTH];
+            for (int p = 0; p < kPagesPerIter; ++p) {
+                if (p < npages) {                             // uniform
+                    f16x8_t pf[NT32];
 #pragma unroll
-                    for (int i = 0; i < NTH; ++i)
-                        pf[i] = *reinterpret_cast<const f16x8_t*>(pbuf(pstep & 1, kb2, i) + lane * 8);
-                    // lane group gq holds keys of page 2*kb2 + gq/2, tile gq&1 (slots 8*(gq&1)..+7)
-                    const uint8_t* vt = pst + A::v_off(2 * kb2 + (gq >> 1)) + (gq & 1) * (D * 8);
+                    for (int r = 0; r < NT32; ++r) pf[r] = *reinterpret_cast<const f16x8_t*>(pbr + (p * NT32 + r) * 1024);
+                    const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vst + p * C::PAGE));
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const int d = w * DW + mt * 16 + li;
-                        const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vt + d * 8));
-#pragma unroll
-                        for (int i = 0; i < NTH; ++i)
-                            o[mt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[i], o[mt][i], 0, 0, 0);
-                    }
+                    for (int r = 0; r < NT32; ++r)
+                        o[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[r], o[r], 0, 0, 0);
                 }
             }
         }
 
-        // ---- Q K^T for this step's page w and this half's tiles
-        f32x4_t sacc[NTH];
-        float kc[4], vsc[4];
-        bool all_visible = false;
-        const int pg0 = pg_begin + it * kPagesPerIter;
-        const int my_page = pg0 + w;
-        const bool page_ok = my_page < pg_end;               // uniform in the wave
-        if (it < n_steps) {
-            const uint8_t* stage = lds + (it % kStages) * A::STAGE;
-            const uint8_t* kpage = stage + A::k_off(w) + li * D;
-            const int swz = k_swizzle<D>(li);
-            u32x4_t kraw[KB / 2];
+        // ---- references.  A wave's flag says some score of its tiles and page
+        // exceeded the row's reference by more than the page's slack (bit 0), and
+        // whether a V scale of the page exceeds 255 (bit 1).  Without bit 0
+        // anywhere no reference moves: every p <= 2^slack of its page and P'
+        // stays inside fp16.  Otherwise the exact step maxima are exchanged, the
+        // rows beyond the step's slack move to them and O is rescaled.
+        const uint32_t flags = __builtin_amdgcn_readfirstlane(((fl0[0] | fl0[1]) | (fl0[2] | fl0[3])) |
+                                                              ((fl1[0] | fl1[1]) | (fl1[2] | fl1[3])));
+        if (flags & 1u) {                                     // rare after the first step
+            const float tau = (flags & 2u) ? 0.0f : kTau;
 #pragma unroll
-            for (int c = 0; c < KB / 2; ++c)
-                kraw[c] = *reinterpret_cast<const u32x4_t*>(kpage + 16 * ((4 * c + gq) ^ swz));
-#pragma unroll
-            for (int i = 0; i < NTH; ++i) sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < KB / 2; ++c) {
-                f16x8_t k0, k1;
-                codes16_to_f16_biased(kraw[c], k0, k1);
-#pragma unroll
-                for (int i = 0; i < NTH; ++i) {
-                    sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[i][2 * c], sacc[i], 0, 0, 0);
-                    sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[i][2 * c + 1], sacc[i], 0, 0, 0);
-                }
+            for (int i = 0; i < NH; ++i) {
+                const float mx = group4_max(fmaxf(fmaxf(zs[i][0], zs[i][1]), fmaxf(zs[i][2], zs[i][3])));
+                if (gq == 0) red[(16 * (t0 + i) + li) * kPagesPerIter + w] = it - 1 <= last_valid ? mx : -INFINITY;
             }
-            // lane (gq, li) holds keys at slots 4*gq + j of page my_page, for row 16*tile + li
-            const u32x2_t ks_raw = *reinterpret_cast<const u32x2_t*>(stage + A::s_off(w) + 8 * gq);
-            const u32x2_t vs_raw = *reinterpret_cast<const u32x2_t*>(stage + A::s_off(w) + 32 + 8 * gq);
+            lds_barrier();
+            bool moved = false;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kc[j] = f16_bits_to_f32(ks_raw[j >> 1] >> (16 * (j & 1))) * zscale;
-                vsc[j] = f16_bits_to_f32(vs_raw[j >> 1] >> (16 * (j & 1)));
-            }
-            // every key of the page is visible to every row (padded rows see q = 0)
-            all_visible = page_ok && my_page * kPage + kPage - 1 <= ctx - dl;
-            float rmax[NTH];
-            if (all_visible) {
-#pragma unroll
-                for (int i = 0; i < NTH; ++i) {
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        sacc[i][j] = (sacc[i][j] - qbias[i]) * kc[j];
-                        mx = fmaxf(mx, sacc[i][j]);
-                    }
-                    rmax[i] = group4_max(mx);
-                }
-            } else {
-                const int key0 = my_page * kPage + 4 * gq;
-#pragma unroll
-                for (int i = 0; i < NTH; ++i) {
-                    const int row = (half + 2 * i) * 16 + li;
-                    const int pos_t = ctx - dl + row / G;     // last key this row may see
-                    const bool row_ok = page_ok && row < rows;
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float zz = (sacc[i][j] - qbias[i]) * kc[j];
-                        sacc[i][j] = (row_ok && key0 + j <= pos_t) ? zz : -INFINITY;
-                        mx = fmaxf(mx, sacc[i][j]);
-                    }
-                    rmax[i] = group4_max(mx);
-                }
-            }
-            // largest V scale of the page (masked slots included: a non-finite or
-            // huge value only makes the rescaling below exact)
-            const float vmax = group4_max(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])));
-            if (gq == 0) {
-#pragma unroll
-                for (int i = 0; i < NTH; ++i) red[((half + 2 * i) * 16 + li) * 4 + w] = rmax[i];
-                if (li == 0 && half == 0) red[A::NT * 16 * 4 + w] = vmax;
-            }
-        }
-        lds_barrier();
-
-        // ---- online softmax with a lazily moved reference.  A row's reference m
-        // only moves when the step's maximum exceeds it by more than tau (log2
-        // units), so p = exp2(z - m) <= 2^tau; tau = 8 unless a V scale of the
-        // step exceeds 255, where P' = p * s_v could leave the fp16 range, and then
-        // tau = 0 (the reference follows the maximum exactly).
-        if (it < n_steps) {
-            const f32x4_t vsm = *reinterpret_cast<const f32x4_t*>(red + A::NT * 16 * 4);
-            const float tau = (fmaxf(fmaxf(vsm[0], vsm[1]), fmaxf(vsm[2], vsm[3])) <= 255.0f) ? 8.0f : 0.0f;
-#pragma unroll
-            for (int i = 0; i < NTH; ++i) {
-                const int row = (half + 2 * i) * 16 + li;
-                const f32x4_t mw = *reinterpret_cast<const f32x4_t*>(red + row * 4);
+            for (int i = 0; i < NH; ++i) {
+                const f32x4_t mw = *reinterpret_cast<const f32x4_t*>(red + (16 * (t0 + i) + li) * kPagesPerIter);
                 const float mstep = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-                const bool move = mstep > m_run[i] + tau;     // -inf + tau stays -inf
-                const float alpha = move ? __builtin_amdgcn_exp2f(m_run[i] - mstep) : 1.0f;
-                if (move) m_run[i] = mstep;
-                if (__builtin_amdgcn_ballot_w64(move) != 0) { // some row of the tile moved
+                const bool fresh = m_ref[i] == -INFINITY;
+                const bool move = fresh ? mstep > -INFINITY : mstep > tau;
+                float alpha = 1.0f;
+                if (move) {
+                    alpha = fresh ? 0.0f : __builtin_amdgcn_exp2f(-mstep);
+                    m_ref[i] = (fresh ? 0.0f : m_ref[i]) + mstep;
+                    nmr[i] = -m_ref[i];
+                    thr[i] = kTau;
                     l_run[i] *= alpha;
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) o[mt][i] *= alpha;
+                    for (int j = 0; j < 4; ++j) zs[i][j] -= mstep;
                 }
-                // rows that have seen no key yet keep m = -inf; their scores are all -inf
-                const float mref = m_run[i] == -INFINITY ? 0.0f : m_run[i];
-                float psum = 0.0f;
-                _Float16 ph[4];
-                if (all_visible) {
+                if (w == 0 && gq == 0) rowv[16 * (t0 + i) + li] = alpha;
+                moved |= __builtin_amdgcn_ballot_w64(move) != 0;
+            }
+            lds_barrier();                                    // factors written, maxima read
+            // O holds P V up to step it - 2, made with the old references
+            if (v < C::PVW) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(sacc[i][j] - mref);
-                        psum += p;
-                        ph[j] = (_Float16)(p * vsc[j]);
-                    }
-                } else {
+                for (int r = 0; r < NT32; ++r) {
+                    const int row = 32 * r + (lane & 31);
+                    const float al = row < 2 * NH * 16 ? rowv[row] : 1.0f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(sacc[i][j] - mref);   // exp2(-inf) = 0
-                        psum += p;
-                        ph[j] = (_Float16)(sacc[i][j] != -INFINITY ? p * vsc[j] : 0.0f);
-                    }
+                    for (int e = 0; e < 16; ++e) o[r][e] *= al;
                 }
-                l_run[i] += psum;                             // this lane's share of the row sum
-                // reader lane (group 2*(w&1) + gq/2, li) of block kb2 = w/2 holds 8 keys;
-                // these 4 are its elements 4*(gq&1)..+3
+            }
+            (void)moved;
+        }
+
+        // ---- softmax of step it - 1: p = exp2(z - m), P' = p * s_v, tile by tile
+        if (do_sm && it - 1 <= last_valid) {
+            _Float16* pb = reinterpret_cast<_Float16*>(lds + C::P_OFF + ((it - 1) & 1) * C::PBUF);
+#pragma unroll
+            for (int i = 0; i < NH; ++i) {
+                const int t = t0 + i;
+                float p[4], pv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[j] = __builtin_amdgcn_exp2f(zs[i][j]);     // exp2(-inf) = 0
+                    pv[j] = p[j] * vsc[j];
+                }
+                l_run[i] += (p[0] + p[1]) + (p[2] + p[3]);
                 u32x2_t packed;
-                packed[0] = (uint32_t)bit_cast<uint16_t>(ph[0]) | ((uint32_t)bit_cast<uint16_t>(ph[1]) << 16);
-                packed[1] = (uint32_t)bit_cast<uint16_t>(ph[2]) | ((uint32_t)bit_cast<uint16_t>(ph[3]) << 16);
-                *reinterpret_cast<u32x2_t*>(pbuf(it & 1, w >> 1, i) + ((2 * (w & 1) + (gq >> 1)) * 16 + li) * 8 +
+                packed[0] = pack_f16x2(pv[0], pv[1]);
+                packed[1] = pack_f16x2(pv[2], pv[3]);
+                // reader lane of the 32-row tile t/2: rows 16 (t&1) + li, keys 8 (gq>>1) + 4 (gq&1) + j
+                *reinterpret_cast<u32x2_t*>(pb + ((w * NT32 + (t >> 1)) * 64 + 32 * (gq >> 1) + 16 * (t & 1) + li) * 8 +
                                             4 * (gq & 1)) = packed;
             }
         }
+
+        // ---- Q K^T of step it for page w and this half's tiles
+        if (it < n) {
+            uint32_t flag = 0;
+            if (it <= last_valid) {
+                const int slot = it & (kRing - 1);
+                const uint8_t* kpage = lds + C::K_OFF + slot * C::SLOT + w * C::PAGE + li * D;
+                const int swz = k_swizzle<D>(li);
+                u32x4_t kraw[KB / 2];
+#pragma unroll
+                for (int c = 0; c < KB / 2; ++c)
+                    kraw[c] = *reinterpret_cast<const u32x4_t*>(kpage + 16 * ((4 * c + gq) ^ swz));
+                // lane (gq, li) holds keys 4 gq + j of the page, row 16 (t0 + i) + li
+                const uint8_t* sc = lds + C::S_OFF + slot * C::SSLOT + w * 64;
+                const u32x2_t ks = *reinterpret_cast<const u32x2_t*>(sc + 8 * gq);
+                const u32x2_t vs = *reinterpret_cast<const u32x2_t*>(sc + 32 + 8 * gq);
+                f32x4_t acc[NH];
+#pragma unroll
+                for (int c = 0; c < KB / 2; ++c) {
+                    f16x8_t k0, k1;
+                    codes16_to_f16_biased(kraw[c], k0, k1);
+                    if (c == 0) qk_chunk<NH, true>(acc, k0, k1, qf[0], qf[1]);
+                    else qk_chunk<NH, false>(acc, k0, k1, qf[2 * c], qf[2 * c + 1]);
+                }
+                float kc[4];
+                kc[0] = f16lo(ks[0]) * zscale;
+                kc[1] = f16hi(ks[0]) * zscale;
+                kc[2] = f16lo(ks[1]) * zscale;
+                kc[3] = f16hi(ks[1]) * zscale;
+                vsc[0] = f16lo(vs[0]);
+                vsc[1] = f16hi(vs[0]);
+                vsc[2] = f16lo(vs[1]);
+                vsc[3] = f16hi(vs[1]);
+                const int key0 = (pg_begin + kPagesPerIter * it + w) * kPage;
+                // every key of the page is visible to every row (padded rows see q = 0)
+                const bool masked = !(key0 + kPage - 1 <= ctx - dl);
+                const int kl = key0 + 4 * gq;
+                if (masked) {                                 // keys past the context carry no V weight
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vsc[j] = kl + j < ctx ? vsc[j] : 0.0f;
+                }
+                // a V scale above 255 leaves no fp16 room above p = 1: slack 0 for this page
+                const bool big =
+                    __builtin_amdgcn_ballot_w64(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])) > 255.0f) != 0;
+                qk_drain<NH>(acc);
+                bool exceed = false;
+#pragma unroll
+                for (int i = 0; i < NH; ++i) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) zs[i][j] = __builtin_fmaf(acc[i][j] - qb[i], kc[j], nmr[i]);
+                    if (masked) {
+                        const int row = 16 * (t0 + i) + li;   // last key the row may see; -1: padded row
+                        const int last_key = row < rows ? ctx - dl + row / G : -1;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) zs[i][j] = kl + j <= last_key ? zs[i][j] : -INFINITY;
+                    }
+                    const float mx = fmaxf(fmaxf(zs[i][0], zs[i][1]), fmaxf(zs[i][2], zs[i][3]));
+                    exceed |= mx > (big ? fminf(thr[i], 0.0f) : thr[i]);
+                }
+                flag = (__builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u) | (big ? 2u : 0u);
+            }
+            if (lane == 0)
+                *reinterpret_cast<uint32_t*>(lds + C::F_OFF + ((it & 1) * kWaves + v) * 4) = flag;
+        }
+        // page id of this wave's next copy: its ring entry was copied at least
+        // three steps ago, so the wait at the top of this step covered it
+        id_next = clamp_page(ring_id(h == 0 ? it + 1 + kKAhead : it + 2));
     }
 
-    // ---- epilogue: row sums across lane groups and the half's four waves, then normalise
+    // ---- epilogue: row sums across lane groups and pages, then normalise
 #pragma unroll
-    for (int i = 0; i < NTH; ++i) {
+    for (int i = 0; i < NH; ++i) {
         const float l = group4_sum(l_run[i]);
-        if (gq == 0) red[((half + 2 * i) * 16 + li) * 4 + w] = l;
+        if (gq == 0) red[(16 * (t0 + i) + li) * kPagesPerIter + w] = l;
+        if (w == 0 && gq == 0) rowv[16 * (t0 + i) + li] = m_ref[i];
     }
     lds_barrier();
+    if (v < C::PVW) {
 #pragma unroll
-    for (int i = 0; i < NTH; ++i) {
-        const int row = (half + 2 * i) * 16 + li;
-        if (row >= rows || !(i + 1 < NTH || last_tile)) continue;
-        const f32x4_t lw = *reinterpret_cast<const f32x4_t*>(red + row * 4);
-        const float l = (lw[0] + lw[1]) + (lw[2] + lw[3]);
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        const int t = row / G, h = g * G + row % G;
-        if (a.out != nullptr) {
-            uint16_t* orow = a.out + (((size_t)b * a.T_max + t) * Hq + h) * D;
+        for (int r = 0; r < NT32; ++r) {
+            const int row = 32 * r + (lane & 31);
+            if (row >= rows) continue;
+            const f32x4_t lw = *reinterpret_cast<const f32x4_t*>(red + row * kPagesPerIter);
+            const float l = (lw[0] + lw[1]) + (lw[2] + lw[3]);
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            const int t = row / G, hq = g * G + row % G;
+            if (a.out != nullptr) {
+                uint16_t* orow = a.out + (((size_t)b * a.T_max + t) * Hq + hq) * D;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int d = w * DW + mt * 16 + 4 * gq;
-                u32x2_t v;
-                v[0] = (uint32_t)f32_to_bf16_rne(o[mt][i][0] * inv) |
-                       ((uint32_t)f32_to_bf16_rne(o[mt][i][1] * inv) << 16);
-                v[1] = (uint32_t)f32_to_bf16_rne(o[mt][i][2] * inv) |
-                       ((uint32_t)f32_to_bf16_rne(o[mt][i][3] * inv) << 16);
-                *reinterpret_cast<u32x2_t*>(orow + d) = v;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * v + 8 * q4 + 4 * (lane >> 5);
+                    u32x2_t x;
+                    x[0] = (uint32_t)f32_to_bf16_rne(o[r][4 * q4] * inv) |
+                           ((uint32_t)f32_to_bf16_rne(o[r][4 * q4 + 1] * inv) << 16);
+                    x[1] = (uint32_t)f32_to_bf16_rne(o[r][4 * q4 + 2] * inv) |
+                           ((uint32_t)f32_to_bf16_rne(o[r][4 * q4 + 3] * inv) << 16);
+                    *reinterpret_cast<u32x2_t*>(orow + d) = x;
+                }
+            } else {
+                const size_t prow = (((size_t)b * Hq + hq) * a.T_max + t) * S + s;
+                float* po = a.part_o + prow * D;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * v + 8 * q4 + 4 * (lane >> 5);
+                    f32x4_t x = {o[r][4 * q4], o[r][4 * q4 + 1], o[r][4 * q4 + 2], o[r][4 * q4 + 3]};
+                    *reinterpret_cast<f32x4_t*>(po + d) = x * inv;
+                }
+                if (v == 0 && lane < 32) {
+                    const float m = rowv[row];
+                    a.part_lse[prow] = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
+                }
             }
-        } else {
-            const size_t prow = (((size_t)b * Hq + h) * a.T_max + t) * S + s;
-            float* po = a.part_o + prow * D;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int d = w * DW + mt * 16 + 4 * gq;
-                *reinterpret_cast<f32x4_t*>(po + d) = o[mt][i] * inv;
-            }
-            if (w == 0 && gq == 0)
-                a.part_lse[prow] = l > 0.0f ? (m_run[i] + log2f(l)) * kLn2 : -INFINITY;
         }
     }
 }
@@ -481,8 +871,9 @@ __device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a,
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kWaves * 64) void verify_partition_kernel(const VerifyArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[Arena<D, G>::TOTAL];
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void verify_partition_kernel(const VerifyArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg<D, G>::TOTAL];
 
     // work item: blockIdx.x = (b * Hkv + g) * S + s  (equal (g, s) of different
     // requests sit S * Hkv apart, so they share an XCD when that is a multiple of 8)
