@@ -166,8 +166,9 @@ def main():
     S_req = args.splits or sda.splash_verify_attn_default_splits(B, Hkv, ctx, P, D)
     S = sda.effective_splits(ctx, P, S_req)
     ws = torch.empty(max(sda.splash_verify_attn_workspace_bytes(B, T, Hq, D, S), 16), dtype=torch.uint8, device=dev)
-    part_o = torch.empty((B, Hq, T, S, D), dtype=torch.float32, device=dev)
-    part_lse = torch.empty((B, Hq, T, S), dtype=torch.float32, device=dev)
+    po_shape, pl_shape = sda.partial_shapes(B, Hq, wl.Hkv, D, S)
+    part_o = torch.empty(po_shape, dtype=torch.float16, device=dev)
+    part_lse = torch.empty(pl_shape, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step(r):

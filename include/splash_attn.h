@@ -62,6 +62,20 @@
  *  - Compiled shapes: P = 16; (D, Hq/Hkv) in {(64, 4), (128, 8), (256, 6)};
  *    T_max <= 16 for verify.  Append accepts D in {64, 128, 256} and any T_max.
  *  - q, out, k_pool, v_pool and the workspace must be 16-byte aligned.
+ *  - Split partials (splash_verify_attn_partition / _splitk_merge, and the
+ *    workspace of splash_verify_attn) use one layout.  With G = Hq / Hkv, a
+ *    (request b, kv head g, split s) owns a block of 16 G rows, row
+ *    r = t * G + (h - g G) for draft t of query head h:
+ *      part_o   fp16  [B][Hkv][S][16 G * D]  each block stored as MFMA tiles
+ *                     [c][R][q][l][e]: c < min(8, D / 32) slices of 32 columns,
+ *                     R < G / 2 tiles of 32 rows, q < 4, lane l < 64, e < 4;
+ *                     element (row r, column d) is at row 32 R + l % 32,
+ *                     d = 32 c + 8 q + 4 (l / 32) + e
+ *      part_lse fp32  [B][Hkv][S][16 G]  natural log
+ *    Each block's rows are the normalised partial o_s scaled by 2^-k and its
+ *    log-sum-exp raised by k ln 2 (k >= 0 chosen per block from its largest V
+ *    scale so that fp16 holds o_s * 2^-k); e^lse * o, which the merge uses, is
+ *    unchanged.  Rows r >= G * draft_lens[b] are neither written nor read.
  */
 #ifndef SPLASH_ATTN_H
 #define SPLASH_ATTN_H
@@ -120,9 +134,10 @@ int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P
 
 /*
  * splash_verify_attn_workspace_bytes -- bytes of device workspace
- * splash_verify_attn needs for num_splits splits (0 when num_splits <= 1):
- * fp32 partial rows [B][Hq][T_max][S][D] followed, at a 256-byte aligned
- * offset, by fp32 log-sum-exps [B][Hq][T_max][S].
+ * splash_verify_attn needs for num_splits splits (0 when num_splits <= 1): the
+ * split partials in the layout above (fp16 part_o for B * 16 Hq rows per
+ * split) followed, at a 256-byte aligned offset, by their fp32 part_lse.
+ * T_max does not change the size.
  */
 size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits);
 
@@ -139,7 +154,8 @@ size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int n
  * max_context_len: host-side upper bound on context_lens (sizes the grid).
  * num_splits: 0 = preset; > 0 forces that many context splits.  When more than
  * one split runs, workspace must hold splash_verify_attn_workspace_bytes(...)
- * bytes (workspace may be NULL when one split runs).  Accumulation is in fp32;
+ * bytes (workspace may be NULL when one split runs).  Accumulation is in fp32
+ * (split partials pass through fp16, a relative rounding of at most 2^-11);
  * the result is deterministic for a given num_splits.
  */
 int splash_verify_attn(const uint16_t* q, uint16_t* out,
@@ -154,11 +170,13 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out,
 /*
  * splash_verify_attn_partition -- the first half of splash_verify_attn on its
  * own: for each context split s (pages [s*L, (s+1)*L) with
- * L = splash_verify_attn_split_pages(...)), write the normalised partial row
- *     part_o[b][h][t][s][:]  = sum_{j in split, j <= pos_t} e^(z_j - m_s) v_hat_j / l_s   (fp32)
- *     part_lse[b][h][t][s]   = m_s + ln l_s   (natural log; -inf and a zero row
- *                                             when the split holds no visible key)
- * for t < draft_lens[b].  For callers that combine partials themselves (for
+ * L = splash_verify_attn_split_pages(...)), write for draft t < draft_lens[b]
+ * and query head h the normalised partial row and its log-sum-exp
+ *     o_s   = sum_{j in split, j <= pos_t} e^(z_j - m_s) v_hat_j / l_s
+ *     lse_s = m_s + ln l_s      (natural log; -inf when the split holds no
+ *                                visible key, and then its row is not written)
+ * into part_o (fp16) and part_lse in the split-partial layout described at the
+ * top of this header.  For callers that combine partials themselves (for
  * example across devices) with splash_verify_attn_splitk_merge.  num_splits
  * must be >= 1 (no preset here); the buffers use exactly num_splits as S.
  */
@@ -169,7 +187,7 @@ int splash_verify_attn_partition(const uint16_t* q,
                                  const int32_t* context_lens, const int32_t* draft_lens,
                                  int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
                                  int max_context_len, float sm_scale, int num_splits,
-                                 float* part_o, float* part_lse, void* stream);
+                                 uint16_t* part_o, float* part_lse, void* stream);
 
 /*
  * splash_verify_attn_split_pages -- pages per split L that the partition uses
@@ -181,18 +199,19 @@ int splash_verify_attn_split_pages(int max_context_len, int P, int num_splits);
 
 /*
  * splash_verify_attn_splitk_merge -- combine S context splits by their
- * log-sum-exps: for t < draft_lens[b],
- *     M = max_s part_lse[b][h][t][s],  w_s = e^(part_lse[b][h][t][s] - M)
- *     out[b][t][h][:] = bf16( sum_s w_s part_o[b][h][t][s][:] / sum_s w_s )
- * summed in a fixed order that depends only on S (the result is
+ * log-sum-exps: for draft t < draft_lens[b] and query head h (row r of kv head
+ * g = h / (Hq/Hkv) in the split-partial layout),
+ *     M = max_s lse_s,  w_s = e^(lse_s - M)
+ *     out[b][t][h][:] = bf16( sum_s w_s o_s[:] / sum_s w_s )
+ * folded in a fixed order that depends only on S (the result is
  * deterministic: the same inputs give the same bits); splits with lse = -inf
  * weigh nothing: their rows may be read (they must lie inside part_o) but
- * never reach the result, whatever they hold.  part_o fp32 [B][Hq][T_max][S][D], part_lse fp32
- * [B][Hq][T_max][S].  Rows t >= draft_lens[b] of out are left untouched.
+ * never reach the result, whatever they hold.  Rows t >= draft_lens[b] of out
+ * are left untouched.  T_max <= 16 and (D, Hq/Hkv) in the compiled set.
  */
-int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse,
+int splash_verify_attn_splitk_merge(const uint16_t* part_o, const float* part_lse,
                                     uint16_t* out, const int32_t* draft_lens,
-                                    int B, int T_max, int Hq, int D, int num_splits,
+                                    int B, int T_max, int Hq, int Hkv, int D, int num_splits,
                                     void* stream);
 
 /* Text for a status code (static storage, never NULL). */

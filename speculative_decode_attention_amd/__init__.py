@@ -70,7 +70,7 @@ def load_library(path: Path | None = None):
     lib.splash_verify_attn_partition.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                  _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
     lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
-    lib.splash_verify_attn_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+    lib.splash_verify_attn_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     lib.splash_status_string.argtypes = [_I]
     lib.splash_status_string.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -238,18 +238,27 @@ def splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, co
     return out
 
 
+def partial_shapes(B, Hq, Hkv, D, num_splits):
+    """Shapes of the split-partial buffers: part_o fp16 [B][Hkv][S][16 G * D] (MFMA
+    tile order inside a block) and part_lse fp32 [B][Hkv][S][16 G], G = Hq / Hkv."""
+    G = Hq // Hkv
+    return (B, Hkv, num_splits, 16 * G * D), (B, Hkv, num_splits, 16 * G)
+
+
 def splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                                  draft_lens, max_context_len, sm_scale, num_splits, part_o,
                                  part_lse, stream=None):
-    """Partial rows per context split: part_o [B][Hq][T_max][S][D], part_lse [B][Hq][T_max][S]."""
+    """Partial rows per context split into part_o (fp16 bits, shapes from
+    partial_shapes) and part_lse (fp32)."""
     torch = _torch()
     B, T_max, Hq, Dq = q.shape
     _dev(q, "q", (torch.bfloat16, torch.int16))
     num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
     maxp = _lens(block_table, context_lens, draft_lens, B)
     S = int(num_splits)
-    _dev(part_o, "part_o", (torch.float32,), (B, Hq, T_max, S, D))
-    _dev(part_lse, "part_lse", (torch.float32,), (B, Hq, T_max, S))
+    po_shape, pl_shape = partial_shapes(B, Hq, Hkv, D, S)
+    _dev(part_o, "part_o", (torch.float16, torch.int16), po_shape)
+    _dev(part_lse, "part_lse", (torch.float32,), pl_shape)
     rc = _lib().splash_verify_attn_partition(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
         block_table.data_ptr(), maxp, context_lens.data_ptr(), draft_lens.data_ptr(), B, T_max,
@@ -259,15 +268,21 @@ def splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, block_tabl
 
 
 def splash_verify_attn_splitk_merge(part_o, part_lse, out, draft_lens, stream=None):
-    """Merge S splits: part_o [B][Hq][T_max][S][D] fp32 -> out [B][T_max][Hq][D] bf16."""
+    """Merge S splits (layout of partial_shapes) -> out [B][T_max][Hq][D] bf16."""
     torch = _torch()
-    B, Hq, T_max, S, D = part_o.shape
-    _dev(part_o, "part_o", (torch.float32,))
-    _dev(part_lse, "part_lse", (torch.float32,), (B, Hq, T_max, S))
-    _dev(out, "out", (torch.bfloat16, torch.int16), (B, T_max, Hq, D))
+    B, T_max, Hq, D = out.shape
+    _dev(out, "out", (torch.bfloat16, torch.int16))
+    if part_lse.dim() != 4 or part_lse.shape[0] != B:
+        raise ValueError("part_lse must be [B][Hkv][S][16 G]")
+    Hkv, S = int(part_lse.shape[1]), int(part_lse.shape[2])
+    if Hkv <= 0 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of the kv head count")
+    po_shape, pl_shape = partial_shapes(B, Hq, Hkv, D, S)
+    _dev(part_o, "part_o", (torch.float16, torch.int16), po_shape)
+    _dev(part_lse, "part_lse", (torch.float32,), pl_shape)
     _dev(draft_lens, "draft_lens", (torch.int32,), (B,))
     rc = _lib().splash_verify_attn_splitk_merge(part_o.data_ptr(), part_lse.data_ptr(),
                                                 out.data_ptr(), draft_lens.data_ptr(), B, T_max,
-                                                Hq, D, S, _stream(stream))
+                                                Hq, Hkv, D, S, _stream(stream))
     _check(rc, "splash_verify_attn_splitk_merge")
     return out

@@ -125,8 +125,10 @@ int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P
 
 size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits) {
     if (B <= 0 || T_max <= 0 || Hq <= 0 || D <= 0 || num_splits <= 1) return 0;
-    const size_t rows = (size_t)B * Hq * T_max * num_splits;
-    return align_up(rows * D * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+    // tiled fp16 partials for 16 drafts of every query head (B * Hkv * 16 G rows
+    // per split = B * 16 Hq), then fp32 log-sum-exps
+    const size_t rows = (size_t)B * 16 * Hq * num_splits;
+    return align_up(rows * D * 2, 256) + align_up(rows * sizeof(float), 256);
 }
 
 int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
@@ -158,13 +160,12 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
     const size_t need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S);
     if (!workspace || !aligned16(workspace)) return SPLASH_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < need) return SPLASH_ERR_WORKSPACE_TOO_SMALL;
-    const size_t rows = (size_t)B * Hq * T_max * S;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align_up(rows * D * sizeof(float), 256));
+    const size_t rows = (size_t)B * 16 * Hq * S;
+    a.part_h = static_cast<uint16_t*>(workspace);
+    a.part_hlse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * D * 2, 256));
     if (launch_verify_partition(a, st) != hipSuccess) return SPLASH_ERR_LAUNCH;
-    MergeArgs m{a.part_o, a.part_lse, out, draft_lens, B, T_max, Hq, D, S};
-    return launch_splitk_merge(m, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
+    TiledMergeArgs m{a.part_h, a.part_hlse, out, draft_lens, B, T_max, Hq, Hkv, D, S};
+    return launch_splitk_merge_tiled(m, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
 }
 
 int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,
@@ -172,7 +173,7 @@ int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const 
                                  const int32_t* block_table, int max_pages_per_seq,
                                  const int32_t* context_lens, const int32_t* draft_lens, int B,
                                  int T_max, int Hq, int Hkv, int D, int P, int num_pages,
-                                 int max_context_len, float sm_scale, int num_splits, float* part_o,
+                                 int max_context_len, float sm_scale, int num_splits, uint16_t* part_o,
                                  float* part_lse, void* stream) {
     int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                                  draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
@@ -189,17 +190,18 @@ int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const 
                                                                                      : SPLASH_ERR_LAUNCH;
 }
 
-int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse, uint16_t* out,
-                                    const int32_t* draft_lens, int B, int T_max, int Hq, int D,
+int splash_verify_attn_splitk_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out,
+                                    const int32_t* draft_lens, int B, int T_max, int Hq, int Hkv, int D,
                                     int num_splits, void* stream) {
     if (!part_o || !part_lse || !out || !draft_lens) return SPLASH_ERR_INVALID_ARGUMENT;
-    if (B < 0 || T_max < 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B < 0 || T_max < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_splits <= 0 || Hq % Hkv != 0)
+        return SPLASH_ERR_INVALID_ARGUMENT;
     if (!aligned16(part_o) || !aligned16(out)) return SPLASH_ERR_INVALID_ARGUMENT;
-    if (D != 64 && D != 128 && D != 256) return SPLASH_ERR_UNSUPPORTED;
+    if (T_max > kMaxVerifyT || !verify_supported(D, Hq / Hkv)) return SPLASH_ERR_UNSUPPORTED;
     if (B == 0 || T_max == 0) return SPLASH_OK;
-    MergeArgs m{part_o, part_lse, out, draft_lens, B, T_max, Hq, D, num_splits};
-    return launch_splitk_merge(m, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
-                                                                                 : SPLASH_ERR_LAUNCH;
+    TiledMergeArgs m{part_o, part_lse, out, draft_lens, B, T_max, Hq, Hkv, D, num_splits};
+    return launch_splitk_merge_tiled(m, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
+                                                                                      : SPLASH_ERR_LAUNCH;
 }
 
 }  // extern "C"

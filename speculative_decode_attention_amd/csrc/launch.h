@@ -26,8 +26,8 @@ struct AppendArgs {
 struct VerifyArgs {
     const uint16_t* q;
     uint16_t* out;             // final bf16 rows (one split)            or nullptr
-    float* part_o;             // fp32 partial rows (several splits)      or nullptr
-    float* part_lse;           // natural-log log-sum-exps per split      or nullptr
+    uint16_t* part_h;          // fp16 tiled partial rows (several splits) or nullptr
+    float* part_hlse;          // their natural-log log-sum-exps, [B][Hkv][S][16 G]
     const int8_t* k_pool;
     const int8_t* v_pool;
     const uint16_t* k_scale;
@@ -43,13 +43,15 @@ struct VerifyArgs {
     int num_pages;             // pool size; page ids are clamped into [0, num_pages)
 };
 
-struct MergeArgs {
-    const float* part_o;
-    const float* part_lse;
+struct TiledMergeArgs {
+    const uint16_t* part_h;
+    const float* part_hlse;
     uint16_t* out;
     const int32_t* draft_lens;
-    int B, T_max, Hq, D, num_splits;
+    int B, T_max, Hq, Hkv, D, num_splits;
 };
+
+
 
 constexpr int kPage = 16;            // tokens per page (the compiled page size)
 constexpr int kPagesPerIter = 4;    // pages a workgroup of the partition kernel takes per step
@@ -58,6 +60,6 @@ bool append_supported(int D);
 bool verify_supported(int D, int G);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream);
-hipError_t launch_splitk_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_splitk_merge_tiled(const TiledMergeArgs& a, hipStream_t stream);
 
 }  // namespace splash

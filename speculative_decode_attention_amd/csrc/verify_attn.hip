@@ -615,6 +615,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 
     f32x4_t zs[NH];                                           // scores of the previous step, relative to m
     float vsc[4];                                             // V scales of the previous step's keys
+    float vmax_seen = 0.0f;                                   // largest V scale of any key this lane scored
 #pragma unroll
     for (int i = 0; i < NH; ++i) zs[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -783,8 +784,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                     for (int j = 0; j < 4; ++j) vsc[j] = kl + j < ctx ? vsc[j] : 0.0f;
                 }
                 // a V scale above 255 leaves no fp16 room above p = 1: slack 0 for this page
-                const bool big =
-                    __builtin_amdgcn_ballot_w64(fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3])) > 255.0f) != 0;
+                const float vmx = fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3]));
+                vmax_seen = fmaxf(vmax_seen, vmx);
+                const bool big = __builtin_amdgcn_ballot_w64(vmx > 255.0f) != 0;
                 qk_drain<NH>(acc);
                 bool exceed = false;
 #pragma unroll
@@ -817,8 +819,26 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         if (gq == 0) red[(16 * (t0 + i) + li) * kPagesPerIter + w] = l;
         if (w == 0 && gq == 0) rowv[16 * (t0 + i) + li] = m_ref[i];
     }
+    float* const vtop = reinterpret_cast<float*>(lds + C::F_OFF);   // the flags are spent by now
+    if (a.out == nullptr) {
+        const float vm = wave_max(vmax_seen);
+        if (lane == 0) vtop[v] = vm;
+    }
     lds_barrier();
     if (v < C::PVW) {
+        // fp16 partials are scaled by 2^-k, k from the largest V scale of the
+        // split, so that |o| <= 127 * that scale * 2^-k stays inside binary16;
+        // k goes into the log-sum-exp, which leaves e^lse * o unchanged
+        int kshift = 0;
+        if (a.out == nullptr) {
+            float vm = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) vm = fmaxf(vm, vtop[i]);
+            const float bound = 127.0f * vm;
+            // floor(log2 bound) from the binary32 exponent field (bound is normal here)
+            const int e2 = (int)((bit_cast<uint32_t>(bound) >> 23) & 0xffu) - 127;
+            kshift = bound < 32768.0f ? 0 : max(0, e2 + 1 - 15);
+        }
 #pragma unroll
         for (int r = 0; r < NT32; ++r) {
             const int row = 32 * r + (lane & 31);
@@ -840,17 +860,22 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                     *reinterpret_cast<u32x2_t*>(orow + d) = x;
                 }
             } else {
-                const size_t prow = (((size_t)b * Hq + hq) * a.T_max + t) * S + s;
-                float* po = a.part_o + prow * D;
+                // tile order [slice v][32-row tile r][q4][lane][4]: every store of
+                // the wave writes 512 contiguous bytes
+                const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
+                uint16_t* dst = a.part_h + blk * (16 * G * D) + (size_t)(((v * C::NT32 + r) * 4) * 64 + lane) * 4;
+                const float sc = __builtin_ldexpf(inv, -kshift);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d = 32 * v + 8 * q4 + 4 * (lane >> 5);
-                    f32x4_t x = {o[r][4 * q4], o[r][4 * q4 + 1], o[r][4 * q4 + 2], o[r][4 * q4 + 3]};
-                    *reinterpret_cast<f32x4_t*>(po + d) = x * inv;
+                    u32x2_t x;
+                    x[0] = pack_f16x2(o[r][4 * q4] * sc, o[r][4 * q4 + 1] * sc);
+                    x[1] = pack_f16x2(o[r][4 * q4 + 2] * sc, o[r][4 * q4 + 3] * sc);
+                    *reinterpret_cast<u32x2_t*>(dst + q4 * 256) = x;
                 }
                 if (v == 0 && lane < 32) {
                     const float m = rowv[row];
-                    a.part_lse[prow] = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
+                    a.part_hlse[blk * (16 * G) + row] =
+                        l > 0.0f ? (m + __builtin_log2f(l) + (float)kshift) * kLn2 : -INFINITY;
                 }
             }
         }
@@ -892,8 +917,7 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int rows = G * dl;
     if (pg_begin >= pg_end) {                                 // empty split: mark it, write no row
         for (int r = threadIdx.x; r < rows; r += kWaves * 64) {
-            const int t = r / G, h = g * G + r % G;
-            a.part_lse[(((size_t)b * a.Hq + h) * a.T_max + t) * S + s] = -INFINITY;
+            a.part_hlse[(((size_t)b * a.Hkv + g) * S + s) * (16 * G) + r] = -INFINITY;
         }
         return;
     }
@@ -901,85 +925,74 @@ void verify_partition_kernel(const VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of S context splits.  One workgroup per output row.  The
-// row's D columns are read as 16-byte groups; the 256 threads are NG groups of
-// D/4 threads, and group sg takes splits sg, sg + NG, ...  Every load of a
-// round (partial rows and log-sum-exps) is issued before any is used, so a
-// round costs one memory latency; S <= NG * kMergeUnroll takes one round.
-// M = max_s lse_s and W = sum_s e^(lse_s - M) are computed by every wave in the
-// same order; the groups' sums are added in group order.  Fixed orders
-// throughout, so the result is deterministic.  A split whose lse is -inf gets
-// weight 0 through a select, so its row (which may hold anything) never
-// reaches the sum.
+// Log-sum-exp merge of the tiled fp16 partials the partition writes
+// (one wave per (request, kv head, 32-row tile, 32-column slice, q4 group):
+// lane l holds row 32 r + l % 32 and 4 columns, and every load of a split is
+// 512 contiguous bytes across the wave).  Splits are taken in batches of
+// kTiledBatch, all loads of a batch issued before any is used, and folded into
+// a running (M, W, acc) in split order, so the result is deterministic for a
+// given S.  A split whose lse is -inf is selected away, never multiplied.
 // ---------------------------------------------------------------------------
-constexpr int kMergeThreads = 256;
-constexpr int kMergeUnroll = 16;
+constexpr int kTiledBatch = 32;
 
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void splitk_merge_kernel(const MergeArgs a) {
-    constexpr int C4 = D / 4;                                 // 16-byte column groups
-    constexpr int NG = kMergeThreads / C4;                    // split groups
+template <int D, int G>
+__global__ __launch_bounds__(64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
+    constexpr int PVW = Cfg<D, G>::PVW, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
     constexpr float kLog2e = 1.4426950408889634f;
-    __shared__ f32x4_t red[NG][C4];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int c4 = tid % C4, sg = tid / C4;
-    const int h = blockIdx.x % a.Hq;
-    const int bt = blockIdx.x / a.Hq;
-    const int t = bt % a.T_max;
-    const int b = bt / a.T_max;
-    if (t >= a.draft_lens[b]) return;
+    int idx = blockIdx.x;
+    const int q4 = idx % 4;
+    idx /= 4;
+    const int v = idx % PVW;
+    idx /= PVW;
+    const int r = idx % NT32;
+    idx /= NT32;
+    const int g = idx % a.Hkv;
+    const int b = idx / a.Hkv;
+    const int lane = threadIdx.x;
+    const int row = 32 * r + (lane & 31);
+    if (row >= G * a.draft_lens[b]) return;
     const int S = a.num_splits;
-    const size_t prow = (((size_t)b * a.Hq + h) * a.T_max + t) * S;
-    const float* lse = a.part_lse + prow;
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part_o + prow * D) + c4;
+    const size_t blk0 = ((size_t)b * a.Hkv + g) * S;
+    const uint16_t* src = a.part_h + blk0 * (ROWS * D) + (size_t)(((v * NT32 + r) * 4 + q4) * 64 + lane) * 4;
+    const float* lse = a.part_hlse + blk0 * ROWS + row;
 
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, W = 0.0f;
-    for (int s0 = 0; s0 < S; s0 += NG * kMergeUnroll) {
-        f32x4_t v[kMergeUnroll];
-        float l[kMergeUnroll];
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kTiledBatch) {
+        u32x2_t x[kTiledBatch];
+        float l[kTiledBatch];
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            const int s = s0 + sg + u * NG;
-            v[u] = s < S ? src[(size_t)s * C4] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kTiledBatch; ++u) {
+            const int sp = s0 + u;
+            x[u] = sp < S ? *reinterpret_cast<const u32x2_t*>(src + (size_t)sp * (ROWS * D)) : u32x2_t{0u, 0u};
+            l[u] = sp < S ? lse[(size_t)sp * ROWS] : -INFINITY;
         }
+        float mb = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            const int s = s0 + sg + u * NG;
-            l[u] = s < S ? lse[s] : -INFINITY;
-        }
-        if (s0 == 0) {                                        // M and W over all splits, per wave
-            float mx = -INFINITY;
-            for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lse[s]);
-            M = wave_max(mx);
-            float ws = 0.0f;
-            if (M != -INFINITY)
-                for (int s = lane; s < S; s += 64) {
-                    const float x = lse[s];
-                    ws += x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
-                }
-            W = wave_sum(ws);
-        }
+        for (int u = 0; u < kTiledBatch; ++u) mb = fmaxf(mb, l[u]);
+        const float mn = fmaxf(M, mb);
+        if (mn == -INFINITY) continue;                        // no split with a visible key yet
+        const float c = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - mn) * kLog2e);
+        W *= c;
+        acc *= c;
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
+        for (int u = 0; u < kTiledBatch; ++u) {
             const bool live = l[u] != -INFINITY;
-            const float w = live ? __builtin_amdgcn_exp2f((l[u] - M) * kLog2e) : 0.0f;
+            const float wt = live ? __builtin_amdgcn_exp2f((l[u] - mn) * kLog2e) : 0.0f;
+            W += wt;
+            const f32x4_t xv = {f16lo(x[u][0]), f16hi(x[u][0]), f16lo(x[u][1]), f16hi(x[u][1])};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += live ? w * v[u][e] : 0.0f;
+            for (int e = 0; e < 4; ++e) acc[e] += live ? wt * xv[e] : 0.0f;
         }
+        M = mn;
     }
-    red[sg][c4] = acc;
-    __syncthreads();
-    if (sg == 0) {
-        f32x4_t x = red[0][c4];
-#pragma unroll
-        for (int g2 = 1; g2 < NG; ++g2) x += red[g2][c4];
-        const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-        u32x2_t o;
-        o[0] = (uint32_t)f32_to_bf16_rne(x[0] * inv) | ((uint32_t)f32_to_bf16_rne(x[1] * inv) << 16);
-        o[1] = (uint32_t)f32_to_bf16_rne(x[2] * inv) | ((uint32_t)f32_to_bf16_rne(x[3] * inv) << 16);
-        *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.T_max + t) * a.Hq + h) * D + 4 * c4) = o;
-    }
+    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    const int t = row / G, hq = g * G + row % G;
+    const int d = 32 * v + 8 * q4 + 4 * (lane >> 5);
+    u32x2_t o;
+    o[0] = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
+    o[1] = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+    *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.T_max + t) * a.Hq + hq) * D + d) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -1004,17 +1017,22 @@ hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_splitk_merge(const MergeArgs& a, hipStream_t stream) {
-    const long blocks = (long)a.B * a.T_max * a.Hq;
+template <int D, int G>
+static hipError_t launch_merge_tiled_dg(const TiledMergeArgs& a, hipStream_t stream) {
+    const long blocks = (long)a.B * a.Hkv * Cfg<D, G>::NT32 * Cfg<D, G>::PVW * 4;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    switch (a.D) {
-        case 64: hipLaunchKernelGGL((splitk_merge_kernel<64>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((splitk_merge_kernel<128>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a); break;
-        case 256: hipLaunchKernelGGL((splitk_merge_kernel<256>), dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), dim3((unsigned)blocks), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
+
+hipError_t launch_splitk_merge_tiled(const TiledMergeArgs& a, hipStream_t stream) {
+    const int G = a.Hq / a.Hkv;
+    if (a.D == 64 && G == 4) return launch_merge_tiled_dg<64, 4>(a, stream);
+    if (a.D == 128 && G == 8) return launch_merge_tiled_dg<128, 8>(a, stream);
+    if (a.D == 256 && G == 6) return launch_merge_tiled_dg<256, 6>(a, stream);
+    return hipErrorInvalidValue;
+}
+
 
 }  // namespace splash

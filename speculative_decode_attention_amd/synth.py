@@ -112,13 +112,16 @@ def place_tokens(k_pool, v_pool, k_scale, v_scale, bt_row, first_pos, k, v, ks, 
 def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq: int, Hkv: int,
                   D: int, num_pages: int, P: int = 16, draft_lens=None, values: str = "quantized",
                   placement: str = "random", shared_prefix: int = 0, nan_pad_q: bool = False,
-                  sm_scale: float | None = None, extra_pages: int = 0) -> Workload:
+                  sm_scale: float | None = None, extra_pages: int = 0, k_mag: float = 1.0,
+                  v_mag: float = 1.0) -> Workload:
     """Build one seeded workload.
 
     values: "quantized" -> fp32 N(0,1) K/V source rows appended through the
     append entry point; "direct" -> int8 codes uniform in [-127, 127] and fp16
     scales uniform in [0.01, 0.05] placed in the pools as given.
     draft_lens: a list, or "random" for uniform draws in 1..T_max.
+    k_mag, v_mag: standard deviations of the "quantized" K and V source rows
+    (large values give peaked scores and V scales beyond fp16's room).
     shared_prefix: tokens (a whole number of pages) that every request shares
     through identical block-table entries.
     """
@@ -137,8 +140,8 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
     own = [int(c) - shared_prefix for c in ctx]
     n_unique = shared_prefix + sum(own)
     if values == "quantized":
-        k_all = rng.standard_normal((n_unique, Hkv, D), dtype=np.float32)
-        v_all = rng.standard_normal((n_unique, Hkv, D), dtype=np.float32)
+        k_all = rng.standard_normal((n_unique, Hkv, D), dtype=np.float32) * np.float32(k_mag)
+        v_all = rng.standard_normal((n_unique, Hkv, D), dtype=np.float32) * np.float32(v_mag)
     elif values == "direct":
         k_all = rng.integers(-127, 128, size=(n_unique, Hkv, D)).astype(np.int8)
         v_all = rng.integers(-127, 128, size=(n_unique, Hkv, D)).astype(np.int8)

@@ -41,10 +41,12 @@ def test_status_strings(lib):
 
 
 def test_workspace_and_split_arithmetic(lib):
-    # fp32 rows [B][Hq][T][S][D] then 256-aligned lse [B][Hq][T][S]
+    # tiled fp16 partials for 16 drafts of every query head per split, then
+    # 256-aligned fp32 log-sum-exps (T_max does not change the size)
     assert sda.splash_verify_attn_workspace_bytes(1, 16, 24, 256, 1) == 0
-    rows = 1 * 24 * 16 * 64
-    want = -(-rows * 256 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    rows = 1 * 16 * 24 * 64
+    want = -(-rows * 256 * 2 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert sda.splash_verify_attn_workspace_bytes(1, 3, 24, 256, 64) == want
     assert sda.splash_verify_attn_workspace_bytes(1, 16, 24, 256, 64) == want
     # pages per split are whole steps of 4 pages
     assert sda.splash_verify_attn_split_pages(32768, 16, 64) == 32
@@ -131,10 +133,12 @@ def test_append_empty_is_a_no_op(lib):
 
 def test_merge_rejects_bad_arguments(lib):
     m = lib.splash_verify_attn_splitk_merge
-    assert m(None, FAKE, FAKE, FAKE, 1, 16, 24, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 256, 0, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 96, 4, None) == sda.SPLASH_ERR_UNSUPPORTED
-    assert m(FAKE, FAKE, FAKE, FAKE, 0, 16, 24, 256, 4, None) == sda.SPLASH_OK
+    assert m(None, FAKE, FAKE, FAKE, 1, 16, 24, 4, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 4, 256, 0, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 5, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 4, 96, 4, None) == sda.SPLASH_ERR_UNSUPPORTED
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 17, 24, 4, 256, 4, None) == sda.SPLASH_ERR_UNSUPPORTED
+    assert m(FAKE, FAKE, FAKE, FAKE, 0, 16, 24, 4, 256, 4, None) == sda.SPLASH_OK
 
 
 def test_partition_rejects_bad_arguments(lib):
@@ -145,7 +149,7 @@ def test_partition_rejects_bad_arguments(lib):
     assert p(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
     args = list(base); args[18] = 0                              # no preset here: splits >= 1
     assert p(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
-    args = list(base); args[19] = FAKE + 8                       # misaligned partial rows
+    args = list(base); args[19] = FAKE + 8                       # misaligned partials
     assert p(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
 
 
