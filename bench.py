@@ -13,10 +13,13 @@ HBM before timing.  Steps rotate over R disjoint replicas of the request's
 pages (identical values, R * 67 MB >= 1 GiB) so that the 256 MB Infinity
 Cache cannot serve the context from one step to the next.
 
-Timing.  Each step is a captured HIP graph (one per replica).  The timed
-replays are queued behind a device-side sleep, so the GPU runs them back to
-back whatever the host's launch rate; events on the launch stream bracket
-exactly K steps.  The partition kernel is also timed alone, K launches back to
+Timing.  Steps are captured in one HIP graph that runs C consecutive steps,
+one per replica (C = the largest divisor of K that is at most R), as a serving
+loop captures the calls of several layers in one graph; a graph launch costs
+several microseconds of idle GPU that a per-call graph would charge to every
+step.  The timed replays are queued behind a device-side sleep, so the GPU
+runs them back to back whatever the host's launch rate; events on the launch
+stream bracket exactly K steps (K / C replays).  The partition kernel is also timed alone, K launches back to
 back between one event pair (queued the same way): its algorithmic bytes over
 its mean launch duration give `roofline.achieved`.
 
@@ -189,36 +192,39 @@ def main():
         step(r)
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()
-    step_graphs, verify_graphs = [], []
-    for fn, graphs in ((step, step_graphs), (verify, verify_graphs)):
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
+    # one graph of C consecutive calls on replicas 0..C-1
+    C = max(d for d in range(1, R + 1) if args.steps % d == 0)
+    graphs = {}
+    for name, fn in (("step", step), ("verify", verify)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for r in range(C):
                 fn(r)
-            graphs.append(g)
+        graphs[name] = g
     torch.cuda.synchronize()
 
     def sleep_ahead(n_items):
         # keep the GPU busy while the host queues n_items (about 40 us of host time each)
         torch.cuda._sleep(int(max(n_items, 1) * 40e-6 * 2.0e9))
 
-    def timed_replays(graphs, n, warm):
-        for i in range(warm):
-            graphs[i % R].replay()
+    def timed_replays(g, n, warm):
+        """Mean time of one call over n calls (n / C replays)."""
+        for _ in range(-(-warm // C)):
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        sleep_ahead(n)
+        sleep_ahead(n // C)
         e0.record()
-        for i in range(n):
-            graphs[i % R].replay()
+        for _ in range(n // C):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    ms_step = timed_replays(step_graphs, args.steps, args.warmup)
+    ms_step = timed_replays(graphs["step"], args.steps, args.warmup)
     step_bytes = verify_bytes(ctx, Hkv, D, T, Hq) + append_bytes(T, Hkv, D)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    us_verify = timed_replays(verify_graphs, args.steps, args.warmup) * 1e3
+    us_verify = timed_replays(graphs["verify"], args.steps, args.warmup) * 1e3
 
     # the partition kernel alone, launched back to back on its stream: one event
     # pair brackets the launches (queued behind a sleep, so the host's launch
@@ -275,7 +281,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "global_batch": B, "seq_len": ctx, "draft_block": T,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8",
-                   "splits": S, "replicas": R, "step_bytes": step_bytes,
+                   "splits": S, "replicas": R, "calls_per_graph": C, "step_bytes": step_bytes,
                    "verify_us_per_call": round(us_verify, 2),
                    "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)},
         "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel<256,6>",

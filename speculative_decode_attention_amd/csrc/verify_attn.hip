@@ -925,20 +925,45 @@ void verify_partition_kernel(const VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the tiled fp16 partials the partition writes
-// (one wave per (request, kv head, 32-row tile, 32-column slice, q4 group):
-// lane l holds row 32 r + l % 32 and 4 columns, and every load of a split is
-// 512 contiguous bytes across the wave).  Splits are taken in batches of
-// kTiledBatch, all loads of a batch issued before any is used, and folded into
-// a running (M, W, acc) in split order, so the result is deterministic for a
-// given S.  A split whose lse is -inf is selected away, never multiplied.
+// Log-sum-exp merge of the tiled fp16 partials the partition writes.  One
+// workgroup of kMergeWaves waves per (request, kv head, 32-row tile, 32-column
+// slice, q4 group): lane l holds row 32 r + l % 32 and 4 columns, so every load
+// of a split is 512 contiguous bytes across a wave.  The waves take contiguous
+// quarters of the splits; each issues the loads of up to kMergeBatch splits
+// before using any (one memory latency for S <= 64) and folds them into a
+// running (M, W, acc) in split order; the quarters are then combined in wave
+// order through LDS.  The result depends only on S.  A split whose lse is -inf
+// is selected away, never multiplied.
 // ---------------------------------------------------------------------------
-constexpr int kTiledBatch = 32;
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 16;
+
+struct MergeState {
+    float M, W;
+    f32x4_t acc;
+};
+
+__device__ __forceinline__ void merge_fold(MergeState& st, float l, const f32x4_t x, float mn) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const bool live = l != -INFINITY;
+    const float wt = live ? __builtin_amdgcn_exp2f((l - mn) * kLog2e) : 0.0f;
+    st.W += wt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.acc[e] += live ? wt * x[e] : 0.0f;
+}
+
+__device__ __forceinline__ void merge_rescale(MergeState& st, float mn) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float c = st.M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((st.M - mn) * kLog2e);
+    st.W *= c;
+    st.acc *= c;
+    st.M = mn;
+}
 
 template <int D, int G>
-__global__ __launch_bounds__(64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
     constexpr int PVW = Cfg<D, G>::PVW, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
-    constexpr float kLog2e = 1.4426950408889634f;
+    __shared__ float xch[kMergeWaves - 1][6][64];
     int idx = blockIdx.x;
     const int q4 = idx % 4;
     idx /= 4;
@@ -948,50 +973,64 @@ __global__ __launch_bounds__(64) void splitk_merge_tiled_kernel(const TiledMerge
     idx /= NT32;
     const int g = idx % a.Hkv;
     const int b = idx / a.Hkv;
-    const int lane = threadIdx.x;
+    const int lim = G * a.draft_lens[b];
+    if (32 * r >= lim) return;                                // uniform: no row of this tile is a draft row
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = 32 * r + (lane & 31);
-    if (row >= G * a.draft_lens[b]) return;
     const int S = a.num_splits;
+    const int per = (S + kMergeWaves - 1) / kMergeWaves;
+    const int s_begin = min(S, wv * per), s_end = min(S, s_begin + per);
     const size_t blk0 = ((size_t)b * a.Hkv + g) * S;
     const uint16_t* src = a.part_h + blk0 * (ROWS * D) + (size_t)(((v * NT32 + r) * 4 + q4) * 64 + lane) * 4;
     const float* lse = a.part_hlse + blk0 * ROWS + row;
 
-    float M = -INFINITY, W = 0.0f;
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += kTiledBatch) {
-        u32x2_t x[kTiledBatch];
-        float l[kTiledBatch];
+    MergeState st{-INFINITY, 0.0f, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    for (int s0 = s_begin; s0 < s_end; s0 += kMergeBatch) {
+        u32x2_t x[kMergeBatch];
+        float l[kMergeBatch];
 #pragma unroll
-        for (int u = 0; u < kTiledBatch; ++u) {
+        for (int u = 0; u < kMergeBatch; ++u) {
             const int sp = s0 + u;
-            x[u] = sp < S ? *reinterpret_cast<const u32x2_t*>(src + (size_t)sp * (ROWS * D)) : u32x2_t{0u, 0u};
-            l[u] = sp < S ? lse[(size_t)sp * ROWS] : -INFINITY;
+            x[u] = sp < s_end ? *reinterpret_cast<const u32x2_t*>(src + (size_t)sp * (ROWS * D)) : u32x2_t{0u, 0u};
+            l[u] = sp < s_end ? lse[(size_t)sp * ROWS] : -INFINITY;
         }
         float mb = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kTiledBatch; ++u) mb = fmaxf(mb, l[u]);
-        const float mn = fmaxf(M, mb);
+        for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, l[u]);
+        const float mn = fmaxf(st.M, mb);
         if (mn == -INFINITY) continue;                        // no split with a visible key yet
-        const float c = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - mn) * kLog2e);
-        W *= c;
-        acc *= c;
+        merge_rescale(st, mn);
 #pragma unroll
-        for (int u = 0; u < kTiledBatch; ++u) {
-            const bool live = l[u] != -INFINITY;
-            const float wt = live ? __builtin_amdgcn_exp2f((l[u] - mn) * kLog2e) : 0.0f;
-            W += wt;
-            const f32x4_t xv = {f16lo(x[u][0]), f16hi(x[u][0]), f16lo(x[u][1]), f16hi(x[u][1])};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += live ? wt * xv[e] : 0.0f;
-        }
-        M = mn;
+        for (int u = 0; u < kMergeBatch; ++u)
+            merge_fold(st, l[u], f32x4_t{f16lo(x[u][0]), f16hi(x[u][0]), f16lo(x[u][1]), f16hi(x[u][1])}, mn);
     }
-    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    if (wv > 0) {
+        xch[wv - 1][0][lane] = st.M;
+        xch[wv - 1][1][lane] = st.W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xch[wv - 1][2 + e][lane] = st.acc[e];
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int k = 0; k < kMergeWaves - 1; ++k) {
+        const float Mk = xch[k][0][lane];
+        const float mn = fmaxf(st.M, Mk);
+        if (mn == -INFINITY) continue;
+        merge_rescale(st, mn);
+        const bool live = Mk != -INFINITY;
+        const float c = live ? __builtin_amdgcn_exp2f((Mk - mn) * 1.4426950408889634f) : 0.0f;
+        st.W += live ? c * xch[k][1][lane] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.acc[e] += live ? c * xch[k][2 + e][lane] : 0.0f;
+    }
+    if (row >= lim) return;
+    const float inv = st.W > 0.0f ? 1.0f / st.W : 0.0f;
     const int t = row / G, hq = g * G + row % G;
     const int d = 32 * v + 8 * q4 + 4 * (lane >> 5);
     u32x2_t o;
-    o[0] = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-    o[1] = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+    o[0] = (uint32_t)f32_to_bf16_rne(st.acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(st.acc[1] * inv) << 16);
+    o[1] = (uint32_t)f32_to_bf16_rne(st.acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(st.acc[3] * inv) << 16);
     *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.T_max + t) * a.Hq + hq) * D + d) = o;
 }
 
@@ -1022,7 +1061,7 @@ static hipError_t launch_merge_tiled_dg(const TiledMergeArgs& a, hipStream_t str
     const long blocks = (long)a.B * a.Hkv * Cfg<D, G>::NT32 * Cfg<D, G>::PVW * 4;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), dim3((unsigned)blocks), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), dim3((unsigned)blocks), dim3(kMergeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
