@@ -67,7 +67,7 @@
  *    (request b, kv head g, split s) owns a block of 16 G rows, row
  *    r = t * G + (h - g G) for draft t of query head h:
  *      part_o   fp16  [B][Hkv][S][16 G * D]  each block stored as MFMA tiles
- *                     [c][R][q][l][e]: c < min(8, D / 32) slices of 32 columns,
+ *                     [c][R][q][l][e]: c < D / 32 slices of 32 columns,
  *                     R < G / 2 tiles of 32 rows, q < 4, lane l < 64, e < 4;
  *                     element (row r, column d) is at row 32 R + l % 32,
  *                     d = 32 c + 8 q + 4 (l / 32) + e

@@ -413,6 +413,7 @@ struct Cfg {
     static constexpr int NI = PAGE / 1024;            // 16-byte copies per lane per page
     static constexpr int PVW = D / 32 < kWaves ? D / 32 : kWaves;   // waves taking part in P V, 32 columns each
     static constexpr int NT32 = (NT + 1) / 2;         // 32-row tiles at 16 drafts
+    static constexpr int NSL = D / 32;                // 32-column slices of a partial block
     static constexpr int SLOT = kPagesPerIter * PAGE; // one step of K (or V) pages
     static constexpr int SSLOT = kPagesPerIter * 64;  // one step of scales: per page 16 K then 16 V (fp16)
     static constexpr int K_OFF = 0;
@@ -466,8 +467,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     constexpr int NT32 = NH;                                  // 32-row tiles in use (P V)
     constexpr int QCHUNKS = 2 * NH * 16 * C::QCH;             // 16-byte chunks of Q converted (padding included)
     constexpr int QI = (QCHUNKS + 64 * kWaves - 1) / (64 * kWaves);   // Q chunks per lane
-    constexpr int STEADY_K = 2 * (NI + 2);                    // copies of a K wave in two steady steps
-    constexpr int STEADY_V = 2 * NI;                          // of a V wave
+    // Copy instructions per pipeline position, the same for every position: a
+    // copy past this wave's pages still runs, on lane 0 only (16 bytes from a
+    // valid page into a ring slot nobody reads), so every wait below is a
+    // constant.  K wave: K rows (NI) + scales, plus the page id from step 0 on;
+    // V wave: V rows from position -1 on.
+    constexpr int KC_START = NI + 1, KC_STEP = NI + 2, VC_STEP = NI;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kLn2 = 0.6931471805599453f;
     constexpr float kTau = 8.0f;                              // lazy-reference slack, log2 units
@@ -484,17 +489,6 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     const int last_valid = (pg_end - pg_begin - 1 - w) >> 2;  // last step with a page w
     const int t0 = h * NH;                                    // first tile of this half
 
-    // copies this wave issues at pipeline position k (k = -3, -2, -1 are the start-up)
-    auto count_at = [&](int k) -> int {
-        int c = 0;
-        if (h == 0) {
-            if (k + kKAhead >= 0 && k + kKAhead <= last_valid) c += NI + 1;
-            if (k >= 0 && k + kIdAhead <= last_valid) c += 1;
-        } else {
-            if (k + 1 >= 0 && k + 1 <= last_valid) c += NI;
-        }
-        return c;
-    };
     // per-lane byte offsets of the K copies inside a page (rows XOR-swizzled by chunk)
     int koff[NI];
 #pragma unroll
@@ -504,14 +498,17 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         koff[i] = h == 0 ? slot * D + 16 * (pc ^ k_swizzle<D>(slot)) : 1024 * i + 16 * lane;
     }
     const int soff = lane < 8 ? 2 * lane : 2 * (lane - 8);    // scale copy: lanes 0-7 K, 8-15 V
-    // K wave: page w's K rows and scales of step j; V wave: its V rows
+    // K wave: page w's K rows and scales of step j; V wave: its V rows.  A
+    // step past this wave's pages copies on lane 0 only (see above).
     auto issue = [&](int j, int page) {
+        const bool on = j <= last_valid || lane == 0;
         const size_t blk = (size_t)page * a.Hkv + g;
         const int8_t* src = (h == 0 ? a.k_pool : a.v_pool) + blk * C::PAGE;
         const uint32_t dst = lds_base + (h == 0 ? C::K_OFF : C::V_OFF) + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) dma16_to_lds(src + koff[i], dst + 1024 * i);
-        if (h == 0 && lane < 16)
+        for (int i = 0; i < NI; ++i)
+            if (on) dma16_to_lds(src + koff[i], dst + 1024 * i);
+        if (h == 0 && lane < 16 && on)
             dma4_to_lds((lane < 8 ? a.k_scale : a.v_scale) + blk * kPage + soff,
                         lds_base + C::S_OFF + (j & (kRing - 1)) * C::SSLOT + w * 64);
     };
@@ -540,10 +537,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     }
 #pragma unroll
     for (int k = -kKAhead; k < 0; ++k) {
-        if (h == 0 && k + kKAhead <= last_valid) issue(k + kKAhead, clamp_page(__builtin_amdgcn_readlane(ids0, k + kKAhead)));
-        if (h == 1 && k + 1 >= 0 && k + 1 <= last_valid) issue(k + 1, clamp_page(__builtin_amdgcn_readlane(ids0, k + 1)));
+        if (h == 0) issue(k + kKAhead, clamp_page(__builtin_amdgcn_readlane(ids0, k + kKAhead)));
+        if (h == 1 && k + 1 >= 0) issue(k + 1, clamp_page(__builtin_amdgcn_readlane(ids0, k + 1)));
     }
-    wait_vmcnt_le(count_at(-3) + count_at(-2) + count_at(-1));   // this lane's Q chunks have landed
+    // this lane's Q chunks have landed (only the copies above may be in flight)
+    if (h == 0) wait_vmcnt<3 * KC_START>(); else wait_vmcnt<VC_STEP>();
     // bf16 -> fp16 in place, each lane its own chunks (exact for 2^-17 <= |q| <= 65504);
     // padded rows become q = 0.  All reads first, then all writes.
     {
@@ -582,18 +580,19 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             for (int i = 0; i < NH; ++i) {
                 const int row = 16 * (t0 + i) + li;
                 const int lc = 8 * (kb >> 1) + 2 * gq + (kb & 1);   // logical 16-byte chunk of d
-                qf[kb][i] = lds_read_agpr(lds_base + C::Q_OFF + row * (2 * D) + 16 * (lc ^ (row % C::QSWZ)));
+                qf[kb][i] = *reinterpret_cast<const f16x8_t*>(lds + C::Q_OFF + row * (2 * D) + 16 * (lc ^ (row % C::QSWZ)));
             }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the AGPR loads above
         f16x8_t k1152;
 #pragma unroll
         for (int e = 0; e < 8; ++e) k1152[e] = (_Float16)1152.0f;
         f32x4_t acc[NH];
-        qk_chunk<NH, true>(acc, k1152, k1152, qf[0], qf[1]);
 #pragma unroll
-        for (int c = 1; c < KB / 2; ++c) qk_chunk<NH, false>(acc, k1152, k1152, qf[2 * c], qf[2 * c + 1]);
-        qk_drain<NH>(acc);
+        for (int i = 0; i < NH; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qf[kb][i], acc[i], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < NH; ++i) qb[i] = acc[i][0];
     }
@@ -626,12 +625,17 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     int id_next = h == 0 ? clamp_page(__builtin_amdgcn_readlane(ids0, kKAhead)) : clamp_page(__builtin_amdgcn_readlane(ids0, 1));
 
     for (int it = 0; it < n + 2; ++it) {
-        // this wave's copies of K(it) or V(it - 2) have landed; the barrier
-        // publishes them, the flags of step it - 1 and the P' tiles of step it - 2
-        if (it >= 2 && it + kIdAhead - 1 <= last_valid) {
-            if (h == 0) wait_vmcnt<STEADY_K>(); else wait_vmcnt<STEADY_V>();
+        // this wave's copies of K(it) or V(it - 2) (position it - 3) have landed:
+        // at most the copies of positions it - 2 and it - 1 are in flight.  The
+        // barrier publishes them, the flags of step it - 1 and the P' tiles of
+        // step it - 2.
+        if (h == 0) {
+            if (it >= 2) wait_vmcnt<2 * KC_STEP>();
+            else if (it == 1) wait_vmcnt<KC_START + KC_STEP>();
+            else wait_vmcnt<2 * KC_START>();
         } else {
-            wait_vmcnt_le(count_at(it - 2) + count_at(it - 1));
+            if (it >= 1) wait_vmcnt<2 * VC_STEP>();
+            else wait_vmcnt<VC_STEP>();
         }
         lds_barrier();
         const bool do_sm = it >= 1 && it <= n;
@@ -642,12 +646,14 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         }
         // ---- copies for later steps
         if (h == 0) {
-            if (it + kKAhead <= last_valid) issue(it + kKAhead, id_next);
-            if (it + kIdAhead <= last_valid && lane == 0)
-                dma4_to_lds(bt + 4 * (it + kIdAhead),
+            issue(it + kKAhead, id_next);
+            // a page id past this wave's pages is read from the split's first
+            // entry, which always exists
+            if (lane == 0)
+                dma4_to_lds(it + kIdAhead <= last_valid ? bt + 4 * (it + kIdAhead) : bt - w,
                             lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + w) * 4);
         } else {
-            if (it + 1 <= last_valid) issue(it + 1, id_next);
+            issue(it + 1, id_next);
         }
 
         // ---- P V of step it - 2: O^T += V^T P'^T for this wave's 32 columns
@@ -760,11 +766,15 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 const u32x2_t vs = *reinterpret_cast<const u32x2_t*>(sc + 32 + 8 * gq);
                 f32x4_t acc[NH];
 #pragma unroll
+                for (int i = 0; i < NH; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
                 for (int c = 0; c < KB / 2; ++c) {
                     f16x8_t k0, k1;
                     codes16_to_f16_biased(kraw[c], k0, k1);
-                    if (c == 0) qk_chunk<NH, true>(acc, k0, k1, qf[0], qf[1]);
-                    else qk_chunk<NH, false>(acc, k0, k1, qf[2 * c], qf[2 * c + 1]);
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * c][i], acc[i], 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * c + 1][i], acc[i], 0, 0, 0);
                 }
                 float kc[4];
                 kc[0] = f16lo(ks[0]) * zscale;
@@ -787,7 +797,6 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 const float vmx = fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3]));
                 vmax_seen = fmaxf(vmax_seen, vmx);
                 const bool big = __builtin_amdgcn_ballot_w64(vmx > 255.0f) != 0;
-                qk_drain<NH>(acc);
                 bool exceed = false;
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
@@ -812,6 +821,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         id_next = clamp_page(ring_id(h == 0 ? it + 1 + kKAhead : it + 2));
     }
 
+    wait_vmcnt<0>();                                          // the lane-0 copies past the pages
     // ---- epilogue: row sums across lane groups and pages, then normalise
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
@@ -962,13 +972,13 @@ __device__ __forceinline__ void merge_rescale(MergeState& st, float mn) {
 
 template <int D, int G>
 __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
-    constexpr int PVW = Cfg<D, G>::PVW, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
+    constexpr int NSL = Cfg<D, G>::NSL, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
     __shared__ float xch[kMergeWaves - 1][6][64];
     int idx = blockIdx.x;
     const int q4 = idx % 4;
     idx /= 4;
-    const int v = idx % PVW;
-    idx /= PVW;
+    const int v = idx % NSL;
+    idx /= NSL;
     const int r = idx % NT32;
     idx /= NT32;
     const int g = idx % a.Hkv;
@@ -1058,7 +1068,7 @@ hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream) {
 
 template <int D, int G>
 static hipError_t launch_merge_tiled_dg(const TiledMergeArgs& a, hipStream_t stream) {
-    const long blocks = (long)a.B * a.Hkv * Cfg<D, G>::NT32 * Cfg<D, G>::PVW * 4;
+    const long blocks = (long)a.B * a.Hkv * Cfg<D, G>::NT32 * Cfg<D, G>::NSL * 4;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), dim3((unsigned)blocks), dim3(kMergeWaves * 64), 0, stream, a);
