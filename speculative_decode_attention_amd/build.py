@@ -19,7 +19,7 @@ HIPCC_FLAGS = [
     "-Wall",
     # never form packed fp32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs, which leaves the AGPRs to the query operands
+    # MFMA accumulators in VGPRs: no AGPR is used, which gives a wave the whole register budget as VGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 

@@ -8,26 +8,23 @@
 // every page across the query heads of its group and all verify tokens (same
 // summary, section "Metal kernels generated to shape"; bnskd.com, "Tech core 2").
 //
-// Work decomposition.  One workgroup of four waves (one per SIMD) per
+// Work decomposition.  One workgroup of eight waves (two per SIMD) per
 // (request b, kv head g, context split s).  Its rows are the R = G * d query
 // rows that share kv head g, ordered r = t * G + hh so that a shorter draft
 // truncates a prefix of rows, padded to tiles of 16; the tile count in use is a
-// compile-time parameter of the body.  Every wave holds the queries of ALL rows
-// in registers, so each page is converted from int8 exactly once per workgroup:
+// compile-time parameter of the body.  Wave (h, w): row half h holds the
+// queries of half the tiles in registers and scores page w of every step
+// against them; for P V the waves split the head dimension.
 //  * The context is walked in steps of kPagesPerIter = 4 pages (64 tokens).
-//    Wave w owns page w of every step: it copies that page's K rows, scales and
-//    V rows HBM -> LDS with 16-byte direct-to-LDS loads, and computes the
-//    scores of all rows against its 16 keys.  For P V the waves split the head
-//    dimension instead (wave w owns columns [w * D/4, (w + 1) * D/4)).
-//  * Copies run three steps ahead: at step i a wave issues K(i + 3) and V(i + 1)
-//    (V is consumed two steps after K).  Rings of four K and four V steps hold
-//    them.  The page ids themselves travel through a small LDS ring, copied six
-//    steps ahead, so no copy waits on a block-table read.  Waits are explicit
-//    per-wave `s_waitcnt vmcnt(n)` with n the exact number of copies issued
-//    since; workgroup barriers wait only on LDS traffic.
+//    Pages go HBM -> LDS with 16-byte direct-to-LDS loads into rings of four
+//    steps: half 0 copies K(i + 3), its scales and the page id of step i + 7
+//    (an LDS ring, so no copy waits on a block-table read), half 1 copies
+//    V(i + 1).  Every step issues the same copy instructions (a copy past the
+//    wave's pages runs on lane 0 only), so each wait is a constant
+//    `s_waitcnt vmcnt(n)`; workgroup barriers wait only on LDS traffic.
 //  * One barrier per step.  Between two barriers a wave runs, for three steps
-//    at once: Q K^T of step i, the softmax of step i - 1 (whose row maxima were
-//    exchanged through the barrier) and P V of step i - 2 (whose P' tiles were).
+//    at once: Q K^T of step i, the softmax of step i - 1 (whose flags crossed
+//    the barrier) and P V of step i - 2 (whose P' tiles did).
 //  * int8 codes x become fp16 with one byte permute: binary16 0x64uu is
 //    1024 + u, and u = x + 128, so the operand holds 1152 + x exactly.  For K the
 //    bias is removed per row after the MFMA (sum_d q_d (1152 + x_d) - 1152 *
@@ -36,13 +33,14 @@
 //  * Scores are kept relative to a per-row reference m that moves lazily: only
 //    when a step's maximum exceeds it by more than tau (log2 units, 8 unless a
 //    V scale of the step exceeds 255, then 0), so p = exp2(z - m) <= 2^tau and
-//    P' = p * s_v stays inside fp16.  The O and row-sum rescale is skipped by
-//    ballot when no row moved.
+//    P' = p * s_v stays inside fp16.  Each wave publishes one flag byte per
+//    step; without a flag no reference moves and nothing is exchanged.
 //  * Q K^T uses v_mfma_f32_16x16x32_f16 (S^T = K Q^T, one 16-key page x 16 rows
 //    per tile); P V uses v_mfma_f32_32x32x16_f16 (O^T = V^T P'^T, 32 columns x
-//    32 rows x one page of keys).
+//    32 rows x 16 keys).  No AGPR is used: a wave then has 256 VGPRs for the
+//    queries, the O accumulators and the working set.
 //  * The epilogue divides by the row sums and writes bf16 rows (one split) or
-//    fp32 partial rows plus their natural-log log-sum-exp (several splits).
+//    fp16 partial tiles with their natural-log log-sum-exp (several splits).
 #include <math.h>
 
 #include "device.h"
@@ -150,257 +148,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
     return bit_cast<uint32_t>(h);
 }
 
-// Q K^T MFMAs (v_mfma_f32_16x16x32_f16) with the query operands read straight
-// from AGPRs, where the queries of all rows stay resident.  Written as inline
-// assembly because the compiler's MFMA selection here reads both sources from
-// VGPRs and would copy every query operand back per instruction.  The wait
-// states the compiler would insert around these MFMAs are written out: two
-// before a block (a VALU write of a source operand just before), none between
-// accumulations into the same registers, and qk_drain() after the last block,
-// before any VALU reads an accumulator (the MFMA result latency).
-// One K chunk of Q K^T for NT row tiles: the K-operand pair (k0, k1) against the
-// query operands of every tile, k0 for all tiles first, then k1, so that
-// accumulations into one tile are NT instructions apart.  FIRST starts the
-// accumulators from zero.  One leading s_nop covers a VALU write of k0/k1 just
-// before the block.
-template <int NT, bool FIRST>
-__device__ __forceinline__ void qk_chunk(f32x4_t* acc, const f16x8_t k0, const f16x8_t k1, const f16x8_t* q0,
-                                         const f16x8_t* q1) {
-    static_assert(NT >= 1 && NT <= 8, "tile count");
-    if constexpr (NT == 1 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %1, %3, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %2, %4, %0"
-            : "=&v"(acc[0])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q1[0]));
-    if constexpr (NT == 1 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %1, %3, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %2, %4, %0"
-            : "+v"(acc[0])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q1[0]));
-    if constexpr (NT == 2 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %2, %4, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %2, %5, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %3, %6, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %3, %7, %1"
-            : "=&v"(acc[0]), "=&v"(acc[1])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q1[0]), "a"(q1[1]));
-    if constexpr (NT == 2 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %2, %4, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %2, %5, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %3, %6, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %3, %7, %1"
-            : "+v"(acc[0]), "+v"(acc[1])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q1[0]), "a"(q1[1]));
-    if constexpr (NT == 3 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %3, %5, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %3, %6, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %3, %7, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %4, %8, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %4, %9, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %4, %10, %2"
-            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]));
-    if constexpr (NT == 3 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %3, %5, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %3, %6, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %3, %7, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %4, %8, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %4, %9, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %4, %10, %2"
-            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]));
-    if constexpr (NT == 4 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %4, %6, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %4, %7, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %4, %8, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %4, %9, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %5, %10, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %5, %11, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %5, %12, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %5, %13, %3"
-            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]));
-    if constexpr (NT == 4 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %4, %6, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %4, %7, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %4, %8, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %4, %9, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %5, %10, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %5, %11, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %5, %12, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %5, %13, %3"
-            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]));
-    if constexpr (NT == 5 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %5, %7, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %5, %8, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %5, %9, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %5, %10, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %5, %11, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %6, %12, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %6, %13, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %6, %14, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %6, %15, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %6, %16, %4"
-            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]));
-    if constexpr (NT == 5 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %5, %7, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %5, %8, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %5, %9, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %5, %10, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %5, %11, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %6, %12, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %6, %13, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %6, %14, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %6, %15, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %6, %16, %4"
-            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]));
-    if constexpr (NT == 6 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %6, %8, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %6, %9, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %6, %10, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %6, %11, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %6, %12, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %6, %13, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %7, %14, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %7, %15, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %7, %16, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %7, %17, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %7, %18, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %7, %19, %5"
-            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]));
-    if constexpr (NT == 6 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %6, %8, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %6, %9, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %6, %10, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %6, %11, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %6, %12, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %6, %13, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %7, %14, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %7, %15, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %7, %16, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %7, %17, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %7, %18, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %7, %19, %5"
-            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]));
-    if constexpr (NT == 7 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %7, %9, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %7, %10, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %7, %11, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %7, %12, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %7, %13, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %7, %14, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %7, %15, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %8, %16, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %8, %17, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %8, %18, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %8, %19, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %8, %20, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %8, %21, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %8, %22, %6"
-            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5]), "=&v"(acc[6])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]));
-    if constexpr (NT == 7 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %7, %9, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %7, %10, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %7, %11, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %7, %12, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %7, %13, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %7, %14, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %7, %15, %6\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %8, %16, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %8, %17, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %8, %18, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %8, %19, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %8, %20, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %8, %21, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %8, %22, %6"
-            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]));
-    if constexpr (NT == 8 && FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %8, %10, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %8, %11, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %8, %12, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %8, %13, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %8, %14, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %8, %15, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %8, %16, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %7, %8, %17, 0\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %9, %18, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %9, %19, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %9, %20, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %9, %21, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %9, %22, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %9, %23, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %9, %24, %6\n\t"
-            "v_mfma_f32_16x16x32_f16 %7, %9, %25, %7"
-            : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(acc[4]), "=&v"(acc[5]), "=&v"(acc[6]), "=&v"(acc[7])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q0[7]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]), "a"(q1[7]));
-    if constexpr (NT == 8 && !FIRST)
-        asm("s_nop 1\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %8, %10, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %8, %11, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %8, %12, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %8, %13, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %8, %14, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %8, %15, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %8, %16, %6\n\t"
-            "v_mfma_f32_16x16x32_f16 %7, %8, %17, %7\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %9, %18, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %9, %19, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %9, %20, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %9, %21, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %9, %22, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %9, %23, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %9, %24, %6\n\t"
-            "v_mfma_f32_16x16x32_f16 %7, %9, %25, %7"
-            : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7])
-            : "v"(k0), "v"(k1), "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q0[4]), "a"(q0[5]), "a"(q0[6]), "a"(q0[7]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]), "a"(q1[3]), "a"(q1[4]), "a"(q1[5]), "a"(q1[6]), "a"(q1[7]));
-}
-
-// Result latency of the last Q K^T MFMAs before VALU reads: 13 wait states (the
-// compiler uses 8 for this instruction).  Every accumulator passes through the
-// statement, so no read of one can be scheduled above it.
-template <int N>
-__device__ __forceinline__ void qk_drain(f32x4_t* acc) {
-#define SPLASH_DRAIN "s_nop 7\n\ts_nop 4"
-    static_assert(N >= 1 && N <= 8, "tile count");
-    if constexpr (N == 1) asm(SPLASH_DRAIN : "+v"(acc[0]));
-    if constexpr (N == 2) asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]));
-    if constexpr (N == 3) asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]));
-    if constexpr (N == 4) asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
-    if constexpr (N == 5)
-        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]));
-    if constexpr (N == 6)
-        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]));
-    if constexpr (N == 7)
-        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
-            "+v"(acc[6]));
-    if constexpr (N == 8)
-        asm(SPLASH_DRAIN : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
-            "+v"(acc[6]), "+v"(acc[7]));
-#undef SPLASH_DRAIN
-}
-
 // Shapes and the LDS arena of one workgroup.
 template <int D, int G>
 struct Cfg {
@@ -441,14 +188,6 @@ template <int D>
 __device__ __forceinline__ int k_swizzle(int slot) {
     constexpr int CH = D / 16;
     return CH >= 8 ? (slot & 7) : ((slot / (8 / CH)) % CH);
-}
-
-// 16 bytes of LDS straight into an AGPR quad.  The compiler does not track this
-// load: it is followed by an explicit s_waitcnt lgkmcnt(0) before any use.
-__device__ __forceinline__ f16x8_t lds_read_agpr(uint32_t addr) {
-    f16x8_t v;
-    asm volatile("ds_read_b128 %0, %1" : "=a"(v) : "v"(addr));
-    return v;
 }
 
 // The body for NTU row tiles in use.  Wave v = 4 h + w: row half h holds tiles
@@ -569,7 +308,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     }
     lds_barrier();
 
-    // ---- this half's Q as fp16 B operands, resident in AGPRs, and the per-row
+    // ---- this half's Q as fp16 B operands, resident in VGPRs, and the per-row
     // K-code bias 1152 * sum_d q_d taken on the MFMA
     f16x8_t qf[KB][NH];
     float qb[NH];
