@@ -229,13 +229,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     const int t0 = h * NH;                                    // first tile of this half
 
     // per-lane byte offsets of the K copies inside a page (rows XOR-swizzled by chunk)
-    int koff[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    auto koff = [&](int i) -> int {
         const int c = 64 * i + lane;
         const int slot = c / C::CH, pc = c % C::CH;
-        koff[i] = h == 0 ? slot * D + 16 * (pc ^ k_swizzle<D>(slot)) : 1024 * i + 16 * lane;
-    }
+        return h == 0 ? slot * D + 16 * (pc ^ k_swizzle<D>(slot)) : 1024 * i + 16 * lane;
+    };
     const int soff = lane < 8 ? 2 * lane : 2 * (lane - 8);    // scale copy: lanes 0-7 K, 8-15 V
     // K wave: page w's K rows and scales of step j; V wave: its V rows.  A
     // step past this wave's pages copies on lane 0 only (see above).
@@ -246,7 +244,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         const uint32_t dst = lds_base + (h == 0 ? C::K_OFF : C::V_OFF) + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            if (on) dma16_to_lds(src + koff[i], dst + 1024 * i);
+            if (on) dma16_to_lds(src + koff(i), dst + 1024 * i);
         if (h == 0 && lane < 16 && on)
             dma4_to_lds((lane < 8 ? a.k_scale : a.v_scale) + blk * kPage + soff,
                         lds_base + C::S_OFF + (j & (kRing - 1)) * C::SSLOT + w * 64);
@@ -258,11 +256,17 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     };
     auto clamp_page = [&](int x) -> int { return min(max(__builtin_amdgcn_readfirstlane(x), 0), a.num_pages - 1); };
 
-    // ---- start-up.  Page ids of steps 0..kIdAhead-1 (plain loads, waited here,
-    // before any copy is in flight), then Q into LDS, then the first copies.
+    // ---- start-up.  Page ids of steps 0..kIdAhead-1 through the scalar cache
+    // (counted apart from the vector copies, so waiting for them holds no copy
+    // back), Q into LDS, then the first copies.
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr btc = (const_i32_ptr)bt;
+    int idj[kIdAhead];
+#pragma unroll
+    for (int j = 0; j < kIdAhead; ++j) idj[j] = j <= last_valid ? btc[4 * j] : 0;
     int ids0 = 0;
-    if (lane < kIdAhead && lane <= last_valid) ids0 = bt[4 * lane];
-    if (h == 0 && lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + w) * 4) = ids0;
+#pragma unroll
+    for (int j = 0; j < kIdAhead; ++j) ids0 = lane == j ? idj[j] : ids0;
 #pragma unroll
     for (int k = 0; k < QI; ++k) {
         const int c = 64 * (v + kWaves * k) + lane;           // Q chunk this lane copies
@@ -274,10 +278,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                          lds_base + C::Q_OFF + 1024 * (v + kWaves * k));
         }
     }
+    if (h == 0 && lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + w) * 4) = ids0;
 #pragma unroll
     for (int k = -kKAhead; k < 0; ++k) {
-        if (h == 0) issue(k + kKAhead, clamp_page(__builtin_amdgcn_readlane(ids0, k + kKAhead)));
-        if (h == 1 && k + 1 >= 0) issue(k + 1, clamp_page(__builtin_amdgcn_readlane(ids0, k + 1)));
+        if (h == 0) issue(k + kKAhead, clamp_page(idj[k + kKAhead]));
+        if (h == 1 && k + 1 >= 0) issue(k + 1, clamp_page(idj[k + 1]));
     }
     // this lane's Q chunks have landed (only the copies above may be in flight)
     if (h == 0) wait_vmcnt<3 * KC_START>(); else wait_vmcnt<VC_STEP>();
@@ -361,7 +366,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     const float zscale = a.sm_scale * kLog2e;
     float* const red = reinterpret_cast<float*>(lds + C::M_OFF);
     float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
-    int id_next = h == 0 ? clamp_page(__builtin_amdgcn_readlane(ids0, kKAhead)) : clamp_page(__builtin_amdgcn_readlane(ids0, 1));
+    int id_next = h == 0 ? clamp_page(idj[kKAhead]) : clamp_page(idj[1]);
 
     for (int it = 0; it < n + 2; ++it) {
         // this wave's copies of K(it) or V(it - 2) (position it - 3) have landed:
@@ -378,11 +383,8 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         }
         lds_barrier();
         const bool do_sm = it >= 1 && it <= n;
-        u32x4_t fl0 = u32x4_t{0u, 0u, 0u, 0u}, fl1 = fl0;
-        if (do_sm) {
-            fl0 = *reinterpret_cast<const u32x4_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves * 4);
-            fl1 = *reinterpret_cast<const u32x4_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves * 4 + 16);
-        }
+        u32x2_t fl = u32x2_t{0u, 0u};
+        if (do_sm) fl = *reinterpret_cast<const u32x2_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves);
         // ---- copies for later steps
         if (h == 0) {
             issue(it + kKAhead, id_next);
@@ -422,8 +424,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         // anywhere no reference moves: every p <= 2^slack of its page and P'
         // stays inside fp16.  Otherwise the exact step maxima are exchanged, the
         // rows beyond the step's slack move to them and O is rescaled.
-        const uint32_t flags = __builtin_amdgcn_readfirstlane(((fl0[0] | fl0[1]) | (fl0[2] | fl0[3])) |
-                                                              ((fl1[0] | fl1[1]) | (fl1[2] | fl1[3])));
+        uint32_t flags = __builtin_amdgcn_readfirstlane(fl[0] | fl[1]);
+        flags |= flags >> 16;
+        flags = (flags | (flags >> 8)) & 3u;
         if (flags & 1u) {                                     // rare after the first step
             const float tau = (flags & 2u) ? 0.0f : kTau;
 #pragma unroll
@@ -553,7 +556,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 flag = (__builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u) | (big ? 2u : 0u);
             }
             if (lane == 0)
-                *reinterpret_cast<uint32_t*>(lds + C::F_OFF + ((it & 1) * kWaves + v) * 4) = flag;
+                *reinterpret_cast<uint8_t*>(lds + C::F_OFF + (it & 1) * kWaves + v) = (uint8_t)flag;
         }
         // page id of this wave's next copy: its ring entry was copied at least
         // three steps ago, so the wait at the top of this step covered it
@@ -658,8 +661,8 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int b = bg / a.Hkv;
 
     const int dl = a.draft_lens[b];
+    const int ctx = a.context_lens[b];                        // both loads in flight together
     if (dl <= 0) return;                                      // request is a no-op
-    const int ctx = a.context_lens[b];
     const int n_pages = (ctx + kPage - 1) / kPage;
     const int pg_begin = s * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_pages);
