@@ -209,9 +209,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     // Copy instructions per pipeline position, the same for every position: a
     // copy past this wave's pages still runs, on lane 0 only (16 bytes from a
     // valid page into a ring slot nobody reads), so every wait below is a
-    // constant.  K wave: K rows (NI) + scales, plus the page id from step 0 on;
-    // V wave: V rows from position -1 on.
-    constexpr int KC_START = NI + 1, KC_STEP = NI + 2, VC_STEP = NI;
+    // constant.  Half 0 issues them all: K rows (NI) + scales, the page id from
+    // step 0 on, and the V rows (NV0 = NI 1 KB parts; half 1 takes NV1 = 0).
+    // Half 1's waves lose issue arbitration to half 0's older waves and set the
+    // pace of every step, so the copies' issue stalls go to half 0.
+    constexpr int NV0 = NI, NV1 = NI - NV0;
+    constexpr int KC_START = NI + 1, KC_STEP = NI + 2;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kLn2 = 0.6931471805599453f;
     constexpr float kTau = 8.0f;                              // lazy-reference slack, log2 units
@@ -232,22 +235,30 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     auto koff = [&](int i) -> int {
         const int c = 64 * i + lane;
         const int slot = c / C::CH, pc = c % C::CH;
-        return h == 0 ? slot * D + 16 * (pc ^ k_swizzle<D>(slot)) : 1024 * i + 16 * lane;
+        return slot * D + 16 * (pc ^ k_swizzle<D>(slot));
     };
     const int soff = lane < 8 ? 2 * lane : 2 * (lane - 8);    // scale copy: lanes 0-7 K, 8-15 V
-    // K wave: page w's K rows and scales of step j; V wave: its V rows.  A
+    // page w's K rows and scales of step j, and V parts [i0, i1) of step j.  A
     // step past this wave's pages copies on lane 0 only (see above).
-    auto issue = [&](int j, int page) {
+    auto issue_k = [&](int j, int page) {
         const bool on = j <= last_valid || lane == 0;
         const size_t blk = (size_t)page * a.Hkv + g;
-        const int8_t* src = (h == 0 ? a.k_pool : a.v_pool) + blk * C::PAGE;
-        const uint32_t dst = lds_base + (h == 0 ? C::K_OFF : C::V_OFF) + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
+        const int8_t* src = a.k_pool + blk * C::PAGE;
+        const uint32_t dst = lds_base + C::K_OFF + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
             if (on) dma16_to_lds(src + koff(i), dst + 1024 * i);
-        if (h == 0 && lane < 16 && on)
+        if (lane < 16 && on)
             dma4_to_lds((lane < 8 ? a.k_scale : a.v_scale) + blk * kPage + soff,
                         lds_base + C::S_OFF + (j & (kRing - 1)) * C::SSLOT + w * 64);
+    };
+    auto issue_v = [&](int j, int page, int i0, int i1) {
+        const bool on = j <= last_valid || lane == 0;
+        const int8_t* src = a.v_pool + ((size_t)page * a.Hkv + g) * C::PAGE + 16 * lane;
+        const uint32_t dst = lds_base + C::V_OFF + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+            if (on) dma16_to_lds(src + 1024 * i, dst + 1024 * i);
     };
     // page id of step j from the id ring, clamped into the pool so that no copy
     // can leave it
@@ -281,11 +292,14 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     if (h == 0 && lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + w) * 4) = ids0;
 #pragma unroll
     for (int k = -kKAhead; k < 0; ++k) {
-        if (h == 0) issue(k + kKAhead, clamp_page(idj[k + kKAhead]));
-        if (h == 1 && k + 1 >= 0) issue(k + 1, clamp_page(idj[k + 1]));
+        if (h == 0) issue_k(k + kKAhead, clamp_page(idj[k + kKAhead]));
+        if (k + 1 >= 0) {
+            if (h == 0) issue_v(k + 1, clamp_page(idj[k + 1]), 0, NV0);
+            else issue_v(k + 1, clamp_page(idj[k + 1]), NV0, NI);
+        }
     }
     // this lane's Q chunks have landed (only the copies above may be in flight)
-    if (h == 0) wait_vmcnt<3 * KC_START>(); else wait_vmcnt<VC_STEP>();
+    if (h == 0) wait_vmcnt<3 * KC_START + NV0>(); else wait_vmcnt<NV1>();
     // bf16 -> fp16 in place, each lane its own chunks (exact for 2^-17 <= |q| <= 65504);
     // padded rows become q = 0.  All reads first, then all writes.
     {
@@ -366,7 +380,8 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     const float zscale = a.sm_scale * kLog2e;
     float* const red = reinterpret_cast<float*>(lds + C::M_OFF);
     float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
-    int id_next = h == 0 ? clamp_page(idj[kKAhead]) : clamp_page(idj[1]);
+    int id_next = h == 0 ? clamp_page(idj[kKAhead]) : clamp_page(idj[1]);   // K (half 0) or V page of the next copies
+    int id_v = clamp_page(idj[1]);                                          // half 0's V page of the next copies
 
     for (int it = 0; it < n + 2; ++it) {
         // this wave's copies of K(it) or V(it - 2) (position it - 3) have landed:
@@ -374,12 +389,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         // barrier publishes them, the flags of step it - 1 and the P' tiles of
         // step it - 2.
         if (h == 0) {
-            if (it >= 2) wait_vmcnt<2 * KC_STEP>();
-            else if (it == 1) wait_vmcnt<KC_START + KC_STEP>();
-            else wait_vmcnt<2 * KC_START>();
+            if (it >= 2) wait_vmcnt<2 * (KC_STEP + NV0)>();
+            else if (it == 1) wait_vmcnt<KC_START + KC_STEP + 2 * NV0>();
+            else wait_vmcnt<2 * KC_START + NV0>();
         } else {
-            if (it >= 1) wait_vmcnt<2 * VC_STEP>();
-            else wait_vmcnt<VC_STEP>();
+            if (it >= 1) wait_vmcnt<2 * NV1>();
+            else wait_vmcnt<NV1>();
         }
         lds_barrier();
         const bool do_sm = it >= 1 && it <= n;
@@ -387,14 +402,15 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         if (do_sm) fl = *reinterpret_cast<const u32x2_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves);
         // ---- copies for later steps
         if (h == 0) {
-            issue(it + kKAhead, id_next);
+            issue_k(it + kKAhead, id_next);
+            issue_v(it + 1, id_v, 0, NV0);
             // a page id past this wave's pages is read from the split's first
             // entry, which always exists
             if (lane == 0)
                 dma4_to_lds(it + kIdAhead <= last_valid ? bt + 4 * (it + kIdAhead) : bt - w,
                             lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + w) * 4);
         } else {
-            issue(it + 1, id_next);
+            issue_v(it + 1, id_next, NV0, NI);
         }
 
         // ---- P V of step it - 2: O^T += V^T P'^T for this wave's 32 columns
@@ -561,6 +577,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         // page id of this wave's next copy: its ring entry was copied at least
         // three steps ago, so the wait at the top of this step covered it
         id_next = clamp_page(ring_id(h == 0 ? it + 1 + kKAhead : it + 2));
+        if (h == 0) id_v = clamp_page(ring_id(it + 2));
     }
 
     wait_vmcnt<0>();                                          // the lane-0 copies past the pages
