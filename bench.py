@@ -78,6 +78,7 @@ def parse():
                     help=f"also run a plain {CALIB_MIB} MiB device copy (for counter calibration)")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
     ap.add_argument("--summarize-traffic", nargs="+", metavar="ARG")
+    ap.add_argument("--oracle-one-thread", metavar="DIR", help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -120,6 +121,8 @@ def main():
         return summarize_stats(args.summarize_stats[0], args.summarize_stats[1:])
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic[:2], args.summarize_traffic[2:])
+    if args.oracle_one_thread:
+        return oracle_one_thread_child(args.oracle_one_thread)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sharding by request, kv head or context is described in DESIGN.md).", file=sys.stderr)
@@ -249,6 +252,26 @@ def main():
         ends[i].record()
     torch.cuda.synchronize()
     part_us_single = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e3
+    # the same launches on one replica only: its pages stay in the 256 MB Infinity Cache
+    sleep_ahead(args.steps)
+    e0.record()
+    for i in range(args.steps):
+        partition(0)
+    e1.record()
+    torch.cuda.synchronize()
+    part_us_warm = e0.elapsed_time(e1) / args.steps * 1e3
+    # practical HBM read ceiling: one read-only pass over 2 GiB (a plain reduction)
+    big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        big.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        big.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbs = big.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
     part_bytes = verify_bytes(ctx, Hkv, D, T, Hq)
     achieved = part_bytes / (part_us * 1e-6) / 1e9
 
@@ -283,6 +306,8 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8",
                    "splits": S, "replicas": R, "calls_per_graph": C, "step_bytes": step_bytes,
                    "verify_us_per_call": round(us_verify, 2),
+                   "partition_us_mall_warm": round(part_us_warm, 3),
+                   "hbm_read_stream_gbs": round(stream_gbs, 1),
                    "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)},
         "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel<256,6>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -315,10 +340,70 @@ def cpu_baseline(wl, seconds):
             break
     sec_per_call = sec / calls
     call_bytes = verify_bytes(int(wl.context_lens[0]), wl.Hkv, wl.D, wl.T_max, wl.Hq)
+    one = oracle_one_thread(wl, pools, rows)
     return {"value": round(call_bytes / sec_per_call / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle",
             "sample": f"{calls} whole verify calls of the benchmark workload ({len(rows)} output rows "
-                      f"each, fp64 C oracle, OpenMP) in {sec:.1f} s: {sec_per_call * 1e3:.0f} ms/call"}
+                      f"each, fp64 C oracle, OpenMP) in {sec:.1f} s: {sec_per_call * 1e3:.0f} ms/call "
+                      f"on {cpu_model()}",
+            "one_thread": one and {"value": round(call_bytes / one["sec_per_call"] / 1e9, 4), "unit": "GB/s",
+                                   "cores": one["threads"],
+                                   "sample": f"{one['calls']} whole call(s) in a child process with "
+                                             f"OMP_NUM_THREADS=1: {one['sec_per_call'] * 1e3:.0f} ms/call"}}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def oracle_one_thread(wl, pools, rows, seconds=4.0):
+    """The same oracle call on one host thread, in a child process (OpenMP reads
+    its thread count at start-up); the inputs travel as .npy files."""
+    import subprocess
+    import tempfile
+    # only the pages the request reads travel, renumbered 0..n-1 (the oracle reads
+    # the pools through the block table alone)
+    n_pages = -(-int(wl.context_lens[0]) // wl.P)
+    used = wl.block_table[0, :n_pages]
+    with tempfile.TemporaryDirectory() as d:
+        arrays = {"q": wl.q, "k_pool": pools[0][used], "v_pool": pools[1][used], "k_scale": pools[2][used],
+                  "v_scale": pools[3][used], "block_table": np.arange(n_pages, dtype=np.int32)[None, :],
+                  "context_lens": wl.context_lens[:1], "draft_lens": wl.draft_lens[:1], "rows": rows}
+        for k, a in arrays.items():
+            np.save(Path(d) / f"{k}.npy", np.ascontiguousarray(a))
+        (Path(d) / "meta.json").write_text(json.dumps({"Hkv": wl.Hkv, "sm_scale": wl.sm_scale, "seconds": seconds}))
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        try:
+            proc = subprocess.run([sys.executable, str(Path(__file__).resolve()), "--oracle-one-thread", d],
+                                  env=env, capture_output=True, text=True, timeout=300)
+        except subprocess.TimeoutExpired:
+            return None
+        if proc.returncode != 0 or not proc.stdout.strip():
+            return None
+        return json.loads(proc.stdout.strip().splitlines()[-1])
+
+
+def oracle_one_thread_child(d):
+    import oracle
+    orc = oracle.load()
+    a = {k: np.load(Path(d) / f"{k}.npy") for k in ("q", "k_pool", "v_pool", "k_scale", "v_scale", "block_table",
+                                                    "context_lens", "draft_lens", "rows")}
+    meta = json.loads((Path(d) / "meta.json").read_text())
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        orc.verify_attn_rows(a["q"], a["k_pool"], a["v_pool"], a["k_scale"], a["v_scale"], a["block_table"],
+                             a["context_lens"], a["draft_lens"], meta["Hkv"], meta["sm_scale"], a["rows"])
+        calls += 1
+        sec = time.perf_counter() - t0
+        if sec >= meta["seconds"]:
+            break
+    print(json.dumps({"sec_per_call": sec / calls, "calls": calls, "threads": orc.num_threads()}), flush=True)
 
 
 # ---------------------------------------------------------------------------

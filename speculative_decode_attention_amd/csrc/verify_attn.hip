@@ -712,13 +712,19 @@ struct MergeState {
     f32x4_t acc;
 };
 
-__device__ __forceinline__ void merge_fold(MergeState& st, float l, const f32x4_t x, float mn) {
+// One split into the running state (mn finite): an empty split's weight is
+// exp2(-inf) = 0 and its rows, which may hold anything, are zeroed bitwise.
+__device__ __forceinline__ void merge_fold(MergeState& st, float l, u32x2_t x, float mn) {
     constexpr float kLog2e = 1.4426950408889634f;
-    const bool live = l != -INFINITY;
-    const float wt = live ? __builtin_amdgcn_exp2f((l - mn) * kLog2e) : 0.0f;
+    const float wt = __builtin_amdgcn_exp2f((l - mn) * kLog2e);
+    const uint32_t keep = l != -INFINITY ? 0xffffffffu : 0u;
+    x[0] &= keep;
+    x[1] &= keep;
     st.W += wt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st.acc[e] += live ? wt * x[e] : 0.0f;
+    st.acc[0] = __builtin_fmaf(wt, f16lo(x[0]), st.acc[0]);
+    st.acc[1] = __builtin_fmaf(wt, f16hi(x[0]), st.acc[1]);
+    st.acc[2] = __builtin_fmaf(wt, f16lo(x[1]), st.acc[2]);
+    st.acc[3] = __builtin_fmaf(wt, f16hi(x[1]), st.acc[3]);
 }
 
 __device__ __forceinline__ void merge_rescale(MergeState& st, float mn) {
@@ -733,18 +739,14 @@ template <int D, int G>
 __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
     constexpr int NSL = Cfg<D, G>::NSL, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
     __shared__ float xch[kMergeWaves - 1][6][64];
-    int idx = blockIdx.x;
-    const int q4 = idx % 4;
-    idx /= 4;
-    const int v = idx % NSL;
-    idx /= NSL;
-    const int r = idx % NT32;
-    idx /= NT32;
-    const int g = idx % a.Hkv;
-    const int b = idx / a.Hkv;
+    // blockIdx.x = (r * NSL + v) * 4 + q4, blockIdx.y = kv head, blockIdx.z = request
+    const int q4 = blockIdx.x % 4;
+    const int v = (blockIdx.x / 4) % NSL;
+    const int r = blockIdx.x / (4 * NSL);
+    const int g = blockIdx.y, b = blockIdx.z;
     const int lim = G * a.draft_lens[b];
     if (32 * r >= lim) return;                                // uniform: no row of this tile is a draft row
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int row = 32 * r + (lane & 31);
     const int S = a.num_splits;
     const int per = (S + kMergeWaves - 1) / kMergeWaves;
@@ -759,10 +761,14 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
         float l[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
-            const int sp = s0 + u;
-            x[u] = sp < s_end ? *reinterpret_cast<const u32x2_t*>(src + (size_t)sp * (ROWS * D)) : u32x2_t{0u, 0u};
-            l[u] = sp < s_end ? lse[(size_t)sp * ROWS] : -INFINITY;
+            // every load is issued (a split past the range re-reads the last
+            // one, in bounds) and then selected away: no branch per load
+            const uint32_t sp = (uint32_t)min(s0 + u, s_end - 1);
+            x[u] = *reinterpret_cast<const u32x2_t*>(src + sp * (uint32_t)(ROWS * D));
+            l[u] = lse[sp * (uint32_t)ROWS];
         }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) l[u] = s0 + u < s_end ? l[u] : -INFINITY;
         float mb = -INFINITY;
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, l[u]);
@@ -771,7 +777,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
         merge_rescale(st, mn);
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u)
-            merge_fold(st, l[u], f32x4_t{f16lo(x[u][0]), f16hi(x[u][0]), f16lo(x[u][1]), f16hi(x[u][1])}, mn);
+            merge_fold(st, l[u], x[u], mn);
     }
     if (wv > 0) {
         xch[wv - 1][0][lane] = st.M;
@@ -787,11 +793,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
         const float mn = fmaxf(st.M, Mk);
         if (mn == -INFINITY) continue;
         merge_rescale(st, mn);
-        const bool live = Mk != -INFINITY;
-        const float c = live ? __builtin_amdgcn_exp2f((Mk - mn) * 1.4426950408889634f) : 0.0f;
-        st.W += live ? c * xch[k][1][lane] : 0.0f;
+        // a wave without a live split holds W = 0 and acc = 0, and gets c = 0
+        const float c = __builtin_amdgcn_exp2f((Mk - mn) * 1.4426950408889634f);
+        st.W = __builtin_fmaf(c, xch[k][1][lane], st.W);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.acc[e] += live ? c * xch[k][2 + e][lane] : 0.0f;
+        for (int e = 0; e < 4; ++e) st.acc[e] = __builtin_fmaf(c, xch[k][2 + e][lane], st.acc[e]);
     }
     if (row >= lim) return;
     const float inv = st.W > 0.0f ? 1.0f / st.W : 0.0f;
@@ -827,10 +833,10 @@ hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream) {
 
 template <int D, int G>
 static hipError_t launch_merge_tiled_dg(const TiledMergeArgs& a, hipStream_t stream) {
-    const long blocks = (long)a.B * a.Hkv * Cfg<D, G>::NT32 * Cfg<D, G>::NSL * 4;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), dim3((unsigned)blocks), dim3(kMergeWaves * 64), 0, stream, a);
+    if (a.B <= 0 || a.Hkv <= 0) return hipSuccess;
+    if (a.B > 65535 || a.Hkv > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid(Cfg<D, G>::NT32 * Cfg<D, G>::NSL * 4, (unsigned)a.Hkv, (unsigned)a.B);
+    hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), grid, dim3(kMergeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
