@@ -62,12 +62,13 @@ KERNEL_SOURCES = ["speculative_decode_attention_amd/csrc/verify_attn.hip",
                   "speculative_decode_attention_amd/csrc/device.h",
                   "speculative_decode_attention_amd/csrc/launch.h"]
 CALIB_MIB = 512
+DEFAULT_STEPS = 200
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's preset")
@@ -436,6 +437,21 @@ def summarize_stats(d, cmd):
     for r in rows:
         print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
               f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    # the partition launches in the order bench.py makes them (default --steps):
+    # graph replays, then three runs of `steps` launches each
+    trace = sorted(csv.DictReader(open(_find(d, "kernel_trace.csv"))), key=lambda r: int(r["Start_Timestamp"]))
+    us = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                   for r in trace if PART_KERNEL in r["Kernel_Name"]])
+    n = DEFAULT_STEPS
+    if len(us) > 3 * n:
+        print("\nPartition launches by phase of the run (kernel trace):\n")
+        print("| phase | launches | mean µs |")
+        print("|---|---:|---:|")
+        for name, seg in (("verify graphs (with the merge)", us[:-3 * n]),
+                          ("back to back, 16 rotating cache replicas (`roofline.mean_launch_us`)", us[-3 * n:-2 * n]),
+                          ("one event pair per launch", us[-2 * n:-n]),
+                          ("back to back, one replica (MALL-warm)", us[-n:])):
+            print(f"| {name} | {len(seg)} | {seg.mean():.2f} |")
 
 
 def _per_dispatch(d, counter):
