@@ -328,9 +328,10 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     lds_barrier();
 
     // ---- this half's Q as fp16 B operands, resident in VGPRs, and the per-row
-    // K-code bias 1152 * sum_d q_d taken on the MFMA
+    // K-code bias -1152 * sum_d q_d, taken on the MFMA; it is the starting value
+    // of every Q K^T accumulator, so the scores come out unbiased
     f16x8_t qf[KB][NH];
-    float qb[NH];
+    f32x4_t nqb[NH];                                          // -1152 * sum_d q_d of each row, as an MFMA C operand
     {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -343,7 +344,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         }
         f16x8_t k1152;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k1152[e] = (_Float16)1152.0f;
+        for (int e = 0; e < 8; ++e) k1152[e] = (_Float16)-1152.0f;
         f32x4_t acc[NH];
 #pragma unroll
         for (int i = 0; i < NH; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -352,7 +353,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 #pragma unroll
             for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qf[kb][i], acc[i], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < NH; ++i) qb[i] = acc[i][0];
+        for (int i = 0; i < NH; ++i) nqb[i] = acc[i];
     }
 
     // per-row state of this half's tiles (row 16 (t0 + i) + li, the same in all lanes of a row)
@@ -371,12 +372,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         for (int e = 0; e < 16; ++e) o[r][e] = 0.0f;
 
     f32x4_t zs[NH];                                           // scores of the previous step, relative to m
-    float vsc[4];                                             // V scales of the previous step's keys
-    float vmax_seen = 0.0f;                                   // largest V scale of any key this lane scored
+    f16x2_t vsh[2];                                           // V scales of the previous step's keys (fp16 pairs)
+    f16x2_t vmax2 = {(_Float16)0.0f, (_Float16)0.0f};         // largest V scales of any key this lane scored
 #pragma unroll
     for (int i = 0; i < NH; ++i) zs[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vsc[j] = 0.0f;
+    for (int j = 0; j < 2; ++j) vsh[j] = f16x2_t{(_Float16)0.0f, (_Float16)0.0f};
     const float zscale = a.sm_scale * kLog2e;
     float* const red = reinterpret_cast<float*>(lds + C::M_OFF);
     float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
@@ -416,21 +417,18 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         // ---- P V of step it - 2: O^T += V^T P'^T for this wave's 32 columns
         if (it >= 2 && v < C::PVW) {
             const int pstep = it - 2;
-            const int npages = min(kPagesPerIter, pg_end - pg_begin - kPagesPerIter * pstep);
             const uint8_t* vst = lds + C::V_OFF + (pstep & (kRing - 1)) * C::SLOT + (lane >> 5) * (D * 8) +
                                  (32 * v + (lane & 31)) * 8;
             const uint8_t* pbr = lds + C::P_OFF + (pstep & 1) * C::PBUF + lane * 16;
 #pragma unroll
             for (int p = 0; p < kPagesPerIter; ++p) {
-                if (p < npages) {                             // uniform
-                    f16x8_t pf[NT32];
+                f16x8_t pf[NT32];
 #pragma unroll
-                    for (int r = 0; r < NT32; ++r) pf[r] = *reinterpret_cast<const f16x8_t*>(pbr + (p * NT32 + r) * 1024);
-                    const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vst + p * C::PAGE));
+                for (int r = 0; r < NT32; ++r) pf[r] = *reinterpret_cast<const f16x8_t*>(pbr + (p * NT32 + r) * 1024);
+                const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vst + p * C::PAGE));
 #pragma unroll
-                    for (int r = 0; r < NT32; ++r)
-                        o[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[r], o[r], 0, 0, 0);
-                }
+                for (int r = 0; r < NT32; ++r)
+                    o[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[r], o[r], 0, 0, 0);
             }
         }
 
@@ -485,22 +483,25 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             (void)moved;
         }
 
-        // ---- softmax of step it - 1: p = exp2(z - m), P' = p * s_v, tile by tile
-        if (do_sm && it - 1 <= last_valid) {
+        // ---- softmax of step it - 1: p = exp2(z - m), P' = p * s_v, tile by tile.
+        // A wave without a page in that step left z = -inf: its P' tiles are zero,
+        // so P V runs over every page of a step without a branch.
+        if (do_sm) {
             _Float16* pb = reinterpret_cast<_Float16*>(lds + C::P_OFF + ((it - 1) & 1) * C::PBUF);
 #pragma unroll
             for (int i = 0; i < NH; ++i) {
                 const int t = t0 + i;
-                float p[4], pv[4];
+                float p[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(zs[i][j]);     // exp2(-inf) = 0
-                    pv[j] = p[j] * vsc[j];
-                }
-                l_run[i] += (p[0] + p[1]) + (p[2] + p[3]);
+                for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(zs[i][j]);     // exp2(-inf) = 0
+                // p rounded once to fp16; the row sum adds exactly these values
+                const f16x2_t h0 = {(_Float16)p[0], (_Float16)p[1]}, h1 = {(_Float16)p[2], (_Float16)p[3]};
+                const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+                l_run[i] = __builtin_amdgcn_fdot2(h0, one2, l_run[i], false);
+                l_run[i] = __builtin_amdgcn_fdot2(h1, one2, l_run[i], false);
                 u32x2_t packed;
-                packed[0] = pack_f16x2(pv[0], pv[1]);
-                packed[1] = pack_f16x2(pv[2], pv[3]);
+                packed[0] = bit_cast<uint32_t>(h0 * vsh[0]);
+                packed[1] = bit_cast<uint32_t>(h1 * vsh[1]);
                 // reader lane of the 32-row tile t/2: rows 16 (t&1) + li, keys 8 (gq>>1) + 4 (gq&1) + j
                 *reinterpret_cast<u32x2_t*>(pb + ((w * NT32 + (t >> 1)) * 64 + 32 * (gq >> 1) + 16 * (t & 1) + li) * 8 +
                                             4 * (gq & 1)) = packed;
@@ -524,7 +525,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 const u32x2_t vs = *reinterpret_cast<const u32x2_t*>(sc + 32 + 8 * gq);
                 f32x4_t acc[NH];
 #pragma unroll
-                for (int i = 0; i < NH; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < NH; ++i) acc[i] = nqb[i];
 #pragma unroll
                 for (int c = 0; c < KB / 2; ++c) {
                     f16x8_t k0, k1;
@@ -539,27 +540,29 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 kc[1] = f16hi(ks[0]) * zscale;
                 kc[2] = f16lo(ks[1]) * zscale;
                 kc[3] = f16hi(ks[1]) * zscale;
-                vsc[0] = f16lo(vs[0]);
-                vsc[1] = f16hi(vs[0]);
-                vsc[2] = f16lo(vs[1]);
-                vsc[3] = f16hi(vs[1]);
+                vsh[0] = bit_cast<f16x2_t>(vs[0]);
+                vsh[1] = bit_cast<f16x2_t>(vs[1]);
                 const int key0 = (pg_begin + kPagesPerIter * it + w) * kPage;
                 // every key of the page is visible to every row (padded rows see q = 0)
                 const bool masked = !(key0 + kPage - 1 <= ctx - dl);
                 const int kl = key0 + 4 * gq;
                 if (masked) {                                 // keys past the context carry no V weight
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) vsc[j] = kl + j < ctx ? vsc[j] : 0.0f;
+                    for (int j = 0; j < 2; ++j) {
+                        const uint32_t keep = (kl + 2 * j < ctx ? 0xffffu : 0u) | (kl + 2 * j + 1 < ctx ? 0xffff0000u : 0u);
+                        vsh[j] = bit_cast<f16x2_t>(bit_cast<uint32_t>(vsh[j]) & keep);
+                    }
                 }
                 // a V scale above 255 leaves no fp16 room above p = 1: slack 0 for this page
-                const float vmx = fmaxf(fmaxf(vsc[0], vsc[1]), fmaxf(vsc[2], vsc[3]));
-                vmax_seen = fmaxf(vmax_seen, vmx);
+                const f16x2_t vm2 = __builtin_elementwise_max(vsh[0], vsh[1]);
+                vmax2 = __builtin_elementwise_max(vmax2, vm2);
+                const float vmx = fmaxf((float)vm2[0], (float)vm2[1]);
                 const bool big = __builtin_amdgcn_ballot_w64(vmx > 255.0f) != 0;
                 bool exceed = false;
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) zs[i][j] = __builtin_fmaf(acc[i][j] - qb[i], kc[j], nmr[i]);
+                    for (int j = 0; j < 4; ++j) zs[i][j] = __builtin_fmaf(acc[i][j], kc[j], nmr[i]);
                     if (masked) {
                         const int row = 16 * (t0 + i) + li;   // last key the row may see; -1: padded row
                         const int last_key = row < rows ? ctx - dl + row / G : -1;
@@ -570,6 +573,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                     exceed |= mx > (big ? fminf(thr[i], 0.0f) : thr[i]);
                 }
                 flag = (__builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u) | (big ? 2u : 0u);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NH; ++i) zs[i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                for (int j = 0; j < 2; ++j) vsh[j] = f16x2_t{(_Float16)0.0f, (_Float16)0.0f};
             }
             if (lane == 0)
                 *reinterpret_cast<uint8_t*>(lds + C::F_OFF + (it & 1) * kWaves + v) = (uint8_t)flag;
@@ -590,7 +598,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     }
     float* const vtop = reinterpret_cast<float*>(lds + C::F_OFF);   // the flags are spent by now
     if (a.out == nullptr) {
-        const float vm = wave_max(vmax_seen);
+        const float vm = wave_max(fmaxf((float)vmax2[0], (float)vmax2[1]));
         if (lane == 0) vtop[v] = vm;
     }
     lds_barrier();
