@@ -10,6 +10,9 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libsplash_attn.so"
 SOURCES = ["abi.hip", "kv_append.hip", "verify_attn.hip"]
+# measurement probe used by bench.py only (not part of the attention library)
+PROBE_LIB = PKG / "libsplash_probe.so"
+PROBE_SOURCES = ["read_ceiling.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -44,12 +47,12 @@ def _run(cmd):
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + proc.stderr[-6000:])
 
 
-def build(out: Path = LIB, extra_flags=()) -> Path:
+def build(out: Path = LIB, extra_flags=(), sources=None) -> Path:
     """Compile every HIP source and link one shared library (always recompiles)."""
     tmp = Path(str(out) + ".tmp")
     with tempfile.TemporaryDirectory(prefix="splash_build_") as td:
         objs = []
-        for src in SOURCES:
+        for src in (SOURCES if sources is None else sources):
             obj = Path(td) / (Path(src).stem + ".o")
             _run([hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c", str(CSRC / src),
                   "-o", str(obj)])
@@ -59,5 +62,11 @@ def build(out: Path = LIB, extra_flags=()) -> Path:
     return out
 
 
+def build_probe() -> Path:
+    """The bandwidth probe library bench.py reports the practical read ceiling with."""
+    return build(PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_probe())

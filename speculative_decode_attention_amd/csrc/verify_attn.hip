@@ -12,33 +12,41 @@
 // (request b, kv head g, context split s).  Its rows are the R = G * d query
 // rows that share kv head g, ordered r = t * G + hh so that a shorter draft
 // truncates a prefix of rows, padded to tiles of 16; the tile count in use is a
-// compile-time parameter of the body.  Wave (h, w): row half h holds the
-// queries of half the tiles in registers and scores page w of every step
-// against them; for P V the waves split the head dimension.
+// compile-time parameter of the body.  The waves take two roles, and wave v and
+// wave v + 4 share a SIMD, so every SIMD runs one of each:
+//  * score waves 0-3: wave 2 h + pp keeps the queries of row half h in
+//    registers, scores pages 2 pp and 2 pp + 1 of every step against them and
+//    runs their softmax one step later;
+//  * output waves 4-7: wave 4 + c copies page c of every step (K rows, scales,
+//    page id, V rows) and owns a quarter of the head dimension of O for P V, so
+//    every V code is converted once.
 //  * The context is walked in steps of kPagesPerIter = 4 pages (64 tokens).
 //    Pages go HBM -> LDS with 16-byte direct-to-LDS loads into rings of four
-//    steps: half 0 copies K(i + 3), its scales and the page id of step i + 7
-//    (an LDS ring, so no copy waits on a block-table read), half 1 copies
-//    V(i + 1).  Every step issues the same copy instructions (a copy past the
-//    wave's pages runs on lane 0 only), so each wait is a constant
-//    `s_waitcnt vmcnt(n)`; workgroup barriers wait only on LDS traffic.
-//  * One barrier per step.  Between two barriers a wave runs, for three steps
-//    at once: Q K^T of step i, the softmax of step i - 1 (whose flags crossed
-//    the barrier) and P V of step i - 2 (whose P' tiles did).
+//    steps: K(i + 3), its scales and the page id of step i + 7 (an LDS ring, so
+//    no copy waits on a block-table read), and V(i + 1).  Every step issues the
+//    same copy instructions (a copy past the split's pages runs on lane 0 only),
+//    so each wait is a constant `s_waitcnt vmcnt(n)`; workgroup barriers wait
+//    only on LDS traffic.
+//  * One barrier per step.  Between two barriers the score waves run the
+//    softmax of step i - 1 (whose flags crossed the barrier) and Q K^T of step
+//    i, the output waves P V of step i - 2 (whose P' tiles crossed it).
 //  * int8 codes x become fp16 with one byte permute: binary16 0x64uu is
 //    1024 + u, and u = x + 128, so the operand holds 1152 + x exactly.  For K the
-//    bias is removed per row after the MFMA (sum_d q_d (1152 + x_d) - 1152 *
-//    sum_d q_d, the second sum also taken on the MFMA); for V it is subtracted
+//    accumulators start at -1152 * sum_d q_d (taken once on the MFMA), so
+//    sum_d q_d (1152 + x_d) comes out unbiased; for V the bias is subtracted
 //    exactly with a packed fp16 add before the MFMA.
 //  * Scores are kept relative to a per-row reference m that moves lazily: only
 //    when a step's maximum exceeds it by more than tau (log2 units, 8 unless a
 //    V scale of the step exceeds 255, then 0), so p = exp2(z - m) <= 2^tau and
-//    P' = p * s_v stays inside fp16.  Each wave publishes one flag byte per
-//    step; without a flag no reference moves and nothing is exchanged.
+//    P' = p * s_v stays inside fp16.  Each score wave publishes one flag byte
+//    per step; without a flag no reference moves and nothing is exchanged.  The
+//    first references are the exact maxima of step 0, exchanged across the
+//    barrier that already separates steps 0 and 1.
 //  * Q K^T uses v_mfma_f32_16x16x32_f16 (S^T = K Q^T, one 16-key page x 16 rows
 //    per tile); P V uses v_mfma_f32_32x32x16_f16 (O^T = V^T P'^T, 32 columns x
 //    32 rows x 16 keys).  No AGPR is used: a wave then has 256 VGPRs for the
-//    queries, the O accumulators and the working set.
+//    queries (score waves) or the O accumulators (output waves) and the working
+//    set.
 //  * The epilogue divides by the row sums and writes bf16 rows (one split) or
 //    fp16 partial tiles with their natural-log log-sum-exp (several splits).
 #include <math.h>
@@ -190,12 +198,17 @@ __device__ __forceinline__ int k_swizzle(int slot) {
     return CH >= 8 ? (slot & 7) : ((slot / (8 / CH)) % CH);
 }
 
-// The body for NTU row tiles in use.  Wave v = 4 h + w: row half h holds tiles
-// [h NH, (h + 1) NH) (NH = ceil(NTU / 2); a tile past NTU is padding with
-// q = 0) and takes page w of every step for Q K^T and the softmax; half 0 copies
-// the K pages, their scales and the page ids, half 1 the V pages.  For P V the
-// waves split the head dimension: wave v owns columns [32 v, 32 v + 32) of all
-// rows, so every V code is converted once.
+// The body for NTU row tiles in use (NH = ceil(NTU / 2) per row half; a tile
+// past NTU is padding with q = 0).  Waves 0-3 score, waves 4-7 accumulate the
+// output; wave v and wave v + 4 share a SIMD, so every SIMD runs one of each and
+// the score wave's conversion and softmax arithmetic overlap the output wave's
+// MFMAs (and the other way round).
+//  * Score wave v = 2 h + pp: row half h keeps the queries of tiles
+//    [h NH, (h + 1) NH) in registers; each step it scores pages 2 pp and
+//    2 pp + 1 against them and runs their softmax one step later.
+//  * Output wave c = v - 4: copies page c of every step (K rows, scales, page
+//    id, V rows) and owns columns [32 c SPW, 32 (c + 1) SPW) of all rows for
+//    P V, so every V code is converted once.
 template <int D, int G, int NTU>
 __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds, const int b, const int g,
                                                const int s, const int dl, const int ctx, const int pg_begin,
@@ -204,16 +217,14 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     constexpr int KB = C::KB, NI = C::NI;
     constexpr int NH = (NTU + 1) / 2;                         // 16-row tiles per half
     constexpr int NT32 = NH;                                  // 32-row tiles in use (P V)
+    constexpr int SPW = C::NSL >= 4 ? C::NSL / 4 : 1;         // 32-column slices per output wave
     constexpr int QCHUNKS = 2 * NH * 16 * C::QCH;             // 16-byte chunks of Q converted (padding included)
     constexpr int QI = (QCHUNKS + 64 * kWaves - 1) / (64 * kWaves);   // Q chunks per lane
-    // Copy instructions per pipeline position, the same for every position: a
-    // copy past this wave's pages still runs, on lane 0 only (16 bytes from a
-    // valid page into a ring slot nobody reads), so every wait below is a
-    // constant.  Half 0 issues them all: K rows (NI) + scales, the page id from
-    // step 0 on, and the V rows (NV0 = NI 1 KB parts; half 1 takes NV1 = 0).
-    // Half 1's waves lose issue arbitration to half 0's older waves and set the
-    // pace of every step, so the copies' issue stalls go to half 0.
-    constexpr int NV0 = NI, NV1 = NI - NV0;
+    // Copy instructions an output wave issues per pipeline position, the same
+    // for every position: a copy past the wave's pages still runs, on lane 0
+    // only (16 bytes from a valid page into a ring slot nobody reads), so every
+    // wait below is a constant.  K rows (NI) + scales + the page id, and the V
+    // rows (NI).
     constexpr int KC_START = NI + 1, KC_STEP = NI + 2;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kLn2 = 0.6931471805599453f;
@@ -221,67 +232,43 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int v = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = v >> 2, w = v & 3;
+    const bool scorer = v < 4;
     const int gq = lane >> 4, li = lane & 15;
     const int rows = G * dl;
     const int Hq = a.Hq, S = a.num_splits;
     const int n = (pg_end - pg_begin + kPagesPerIter - 1) / kPagesPerIter;   // steps
-    const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq + pg_begin + w;   // + 4 j
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-    const int last_valid = (pg_end - pg_begin - 1 - w) >> 2;  // last step with a page w
-    const int t0 = h * NH;                                    // first tile of this half
+    // last step holding page p of a step
+    auto last_step = [&](int p) -> int { return (pg_end - pg_begin - 1 - p) >> 2; };
+    float* const red = reinterpret_cast<float*>(lds + C::M_OFF);     // [row][page pair]
+    float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
+    float* const vtop = reinterpret_cast<float*>(lds + C::F_OFF);    // after the loop: V scale maxima
+    // flags of step j: one byte per score wave (bytes 4-7 stay zero)
+    auto read_flags = [&](int j) -> uint32_t {
+        const u32x2_t fl = *reinterpret_cast<const u32x2_t*>(lds + C::F_OFF + (j & 1) * kWaves);
+        uint32_t f = __builtin_amdgcn_readfirstlane(fl[0] | fl[1]);
+        f |= f >> 16;
+        return (f | (f >> 8)) & 3u;
+    };
 
-    // per-lane byte offsets of the K copies inside a page (rows XOR-swizzled by chunk)
-    auto koff = [&](int i) -> int {
-        const int c = 64 * i + lane;
-        const int slot = c / C::CH, pc = c % C::CH;
-        return slot * D + 16 * (pc ^ k_swizzle<D>(slot));
-    };
-    const int soff = lane < 8 ? 2 * lane : 2 * (lane - 8);    // scale copy: lanes 0-7 K, 8-15 V
-    // page w's K rows and scales of step j, and V parts [i0, i1) of step j.  A
-    // step past this wave's pages copies on lane 0 only (see above).
-    auto issue_k = [&](int j, int page) {
-        const bool on = j <= last_valid || lane == 0;
-        const size_t blk = (size_t)page * a.Hkv + g;
-        const int8_t* src = a.k_pool + blk * C::PAGE;
-        const uint32_t dst = lds_base + C::K_OFF + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            if (on) dma16_to_lds(src + koff(i), dst + 1024 * i);
-        if (lane < 16 && on)
-            dma4_to_lds((lane < 8 ? a.k_scale : a.v_scale) + blk * kPage + soff,
-                        lds_base + C::S_OFF + (j & (kRing - 1)) * C::SSLOT + w * 64);
-    };
-    auto issue_v = [&](int j, int page, int i0, int i1) {
-        const bool on = j <= last_valid || lane == 0;
-        const int8_t* src = a.v_pool + ((size_t)page * a.Hkv + g) * C::PAGE + 16 * lane;
-        const uint32_t dst = lds_base + C::V_OFF + (j & (kRing - 1)) * C::SLOT + w * C::PAGE;
-#pragma unroll
-        for (int i = i0; i < i1; ++i)
-            if (on) dma16_to_lds(src + 1024 * i, dst + 1024 * i);
-    };
-    // page id of step j from the id ring, clamped into the pool so that no copy
-    // can leave it
-    auto ring_id = [&](int j) -> int {
-        return *reinterpret_cast<const int*>(lds + C::ID_OFF + ((j & (kIdRing - 1)) * kPagesPerIter + w) * 4);
-    };
-    auto clamp_page = [&](int x) -> int { return min(max(__builtin_amdgcn_readfirstlane(x), 0), a.num_pages - 1); };
-
-    // ---- start-up.  Page ids of steps 0..kIdAhead-1 through the scalar cache
-    // (counted apart from the vector copies, so waiting for them holds no copy
-    // back), Q into LDS, then the first copies.
+    // ---- start-up, output waves: page ids of steps 0..kIdAhead-1 of page c
+    // through the scalar cache (counted apart from the vector copies, so waiting
+    // for them holds no copy back)
+    const int c = v & 3;                                      // output wave: page and column quarter
+    const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq + pg_begin + c;   // + 4 j
+    const int last_c = last_step(c);
     typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-    const const_i32_ptr btc = (const_i32_ptr)bt;
     int idj[kIdAhead];
+    if (!scorer) {
+        const const_i32_ptr btc = (const_i32_ptr)bt;
 #pragma unroll
-    for (int j = 0; j < kIdAhead; ++j) idj[j] = j <= last_valid ? btc[4 * j] : 0;
-    int ids0 = 0;
-#pragma unroll
-    for (int j = 0; j < kIdAhead; ++j) ids0 = lane == j ? idj[j] : ids0;
+        for (int j = 0; j < kIdAhead; ++j) idj[j] = j <= last_c ? btc[4 * j] : 0;
+    }
+    // every wave copies its share of Q into LDS
 #pragma unroll
     for (int k = 0; k < QI; ++k) {
-        const int c = 64 * (v + kWaves * k) + lane;           // Q chunk this lane copies
-        const int row = c / C::QCH, pc = c % C::QCH;
+        const int ch = 64 * (v + kWaves * k) + lane;          // Q chunk this lane copies
+        const int row = ch / C::QCH, pc = ch % C::QCH;
         if (row < rows) {
             const int lc = pc ^ (row % C::QSWZ);
             const int t = row / G, hq = g * G + row % G;
@@ -289,372 +276,521 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                          lds_base + C::Q_OFF + 1024 * (v + kWaves * k));
         }
     }
-    if (h == 0 && lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + w) * 4) = ids0;
+
+    // per-lane byte offsets of the K copies inside a page (rows XOR-swizzled by chunk)
+    auto koff = [&](int i) -> int {
+        const int ch = 64 * i + lane;
+        const int slot = ch / C::CH, pc = ch % C::CH;
+        return slot * D + 16 * (pc ^ k_swizzle<D>(slot));
+    };
+    const int soff = lane < 8 ? 2 * lane : 2 * (lane - 8);    // scale copy: lanes 0-7 K, 8-15 V
+    // page c's K rows and scales of step j, and its V rows.  A step past the
+    // page copies on lane 0 only (see above).
+    auto issue_k = [&](int j, int page) {
+        const bool on = j <= last_c || lane == 0;
+        const size_t blk = (size_t)page * a.Hkv + g;
+        const int8_t* src = a.k_pool + blk * C::PAGE;
+        const uint32_t dst = lds_base + C::K_OFF + (j & (kRing - 1)) * C::SLOT + c * C::PAGE;
 #pragma unroll
-    for (int k = -kKAhead; k < 0; ++k) {
-        if (h == 0) issue_k(k + kKAhead, clamp_page(idj[k + kKAhead]));
-        if (k + 1 >= 0) {
-            if (h == 0) issue_v(k + 1, clamp_page(idj[k + 1]), 0, NV0);
-            else issue_v(k + 1, clamp_page(idj[k + 1]), NV0, NI);
-        }
+        for (int i = 0; i < NI; ++i)
+            if (on) dma16_to_lds(src + koff(i), dst + 1024 * i);
+        if (lane < 16 && on)
+            dma4_to_lds((lane < 8 ? a.k_scale : a.v_scale) + blk * kPage + soff,
+                        lds_base + C::S_OFF + (j & (kRing - 1)) * C::SSLOT + c * 64);
+    };
+    auto issue_v = [&](int j, int page) {
+        const bool on = j <= last_c || lane == 0;
+        const int8_t* src = a.v_pool + ((size_t)page * a.Hkv + g) * C::PAGE + 16 * lane;
+        const uint32_t dst = lds_base + C::V_OFF + (j & (kRing - 1)) * C::SLOT + c * C::PAGE;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (on) dma16_to_lds(src + 1024 * i, dst + 1024 * i);
+    };
+    // page id of step j from the id ring, clamped into the pool so that no copy
+    // can leave it
+    auto ring_id = [&](int j) -> int {
+        return *reinterpret_cast<const int*>(lds + C::ID_OFF + ((j & (kIdRing - 1)) * kPagesPerIter + c) * 4);
+    };
+    auto clamp_page = [&](int x) -> int { return min(max(__builtin_amdgcn_readfirstlane(x), 0), a.num_pages - 1); };
+
+    if (!scorer) {
+        int ids0 = 0;
+#pragma unroll
+        for (int j = 0; j < kIdAhead; ++j) ids0 = lane == j ? idj[j] : ids0;
+        if (lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + c) * 4) = ids0;
+        if (c == 0 && lane < 2 * kWaves / 4)                  // both flag buffers start clear
+            *reinterpret_cast<uint32_t*>(lds + C::F_OFF + 4 * lane) = 0u;
+#pragma unroll
+        for (int j = 0; j < kKAhead; ++j) issue_k(j, clamp_page(idj[j]));
+        issue_v(0, clamp_page(idj[0]));
+        // this lane's Q chunks have landed (only the page copies may be in flight)
+        wait_vmcnt<3 * KC_START + NI>();
+    } else {
+        wait_vmcnt<0>();
     }
-    // this lane's Q chunks have landed (only the copies above may be in flight)
-    if (h == 0) wait_vmcnt<3 * KC_START + NV0>(); else wait_vmcnt<NV1>();
     // bf16 -> fp16 in place, each lane its own chunks (exact for 2^-17 <= |q| <= 65504);
     // padded rows become q = 0.  All reads first, then all writes.
     {
         u32x4_t raw[QI];
 #pragma unroll
         for (int k = 0; k < QI; ++k) {
-            const int c = 64 * (v + kWaves * k) + lane;
-            raw[k] = (QCHUNKS % (64 * kWaves) == 0 || c < QCHUNKS)
-                         ? *reinterpret_cast<const u32x4_t*>(lds + C::Q_OFF + 16 * c)
+            const int ch = 64 * (v + kWaves * k) + lane;
+            raw[k] = (QCHUNKS % (64 * kWaves) == 0 || ch < QCHUNKS)
+                         ? *reinterpret_cast<const u32x4_t*>(lds + C::Q_OFF + 16 * ch)
                          : u32x4_t{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int k = 0; k < QI; ++k) {
-            const int c = 64 * (v + kWaves * k) + lane;
-            const uint32_t okmask = c / C::QCH < rows ? 0xffffffffu : 0u;
+            const int ch = 64 * (v + kWaves * k) + lane;
+            const uint32_t okmask = ch / C::QCH < rows ? 0xffffffffu : 0u;
             u32x4_t hv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t x = raw[k][e] & okmask;
                 hv[e] = pack_f16x2(bit_cast<float>(x << 16), bit_cast<float>(x & 0xffff0000u));
             }
-            if (QCHUNKS % (64 * kWaves) == 0 || c < QCHUNKS)
-                *reinterpret_cast<u32x4_t*>(lds + C::Q_OFF + 16 * c) = hv;
+            if (QCHUNKS % (64 * kWaves) == 0 || ch < QCHUNKS)
+                *reinterpret_cast<u32x4_t*>(lds + C::Q_OFF + 16 * ch) = hv;
         }
     }
     lds_barrier();
 
-    // ---- this half's Q as fp16 B operands, resident in VGPRs, and the per-row
-    // K-code bias -1152 * sum_d q_d, taken on the MFMA; it is the starting value
-    // of every Q K^T accumulator, so the scores come out unbiased
-    f16x8_t qf[KB][NH];
-    f32x4_t nqb[NH];                                          // -1152 * sum_d q_d of each row, as an MFMA C operand
-    {
+    if (scorer) {
+        // ================= score waves =================
+        const int h = v >> 1, pp = v & 1;
+        const int t0 = h * NH;                                // first tile of this half
+        const int lv0 = last_step(2 * pp), lv1 = last_step(2 * pp + 1);
+        // this half's Q as fp16 B operands, resident in VGPRs, and the per-row
+        // K-code bias -1152 * sum_d q_d, taken on the MFMA; it is the starting
+        // value of every Q K^T accumulator, so the scores come out unbiased.
+        // Lane (gq, li) holds d in [8 lc, 8 lc + 8) of row 16 (t0 + i) + li for
+        // contraction block kb, the same d as the K codes it meets.
+        f16x8_t qf[KB][NH];
+        f32x4_t nqb[NH];
+        {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const int row = 16 * (t0 + i) + li;
-                const int lc = 8 * (kb >> 1) + 2 * gq + (kb & 1);   // logical 16-byte chunk of d
-                qf[kb][i] = *reinterpret_cast<const f16x8_t*>(lds + C::Q_OFF + row * (2 * D) + 16 * (lc ^ (row % C::QSWZ)));
+                for (int i = 0; i < NH; ++i) {
+                    const int row = 16 * (t0 + i) + li;
+                    const int lc = 8 * (kb >> 1) + 2 * gq + (kb & 1);
+                    qf[kb][i] = *reinterpret_cast<const f16x8_t*>(lds + C::Q_OFF + row * (2 * D) + 16 * (lc ^ (row % C::QSWZ)));
+                }
             }
+            f16x8_t k1152;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) k1152[e] = (_Float16)-1152.0f;
+#pragma unroll
+            for (int i = 0; i < NH; ++i) nqb[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < NH; ++i) nqb[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qf[kb][i], nqb[i], 0, 0, 0);
         }
-        f16x8_t k1152;
+        // per-row state of this half's tiles (row 16 (t0 + i) + li, the same in all lanes of a row)
+        float m_ref[NH], nmr[NH], l_run[NH], thr[NH];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k1152[e] = (_Float16)-1152.0f;
-        f32x4_t acc[NH];
-#pragma unroll
-        for (int i = 0; i < NH; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qf[kb][i], acc[i], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < NH; ++i) nqb[i] = acc[i];
-    }
-
-    // per-row state of this half's tiles (row 16 (t0 + i) + li, the same in all lanes of a row)
-    float m_ref[NH], nmr[NH], l_run[NH], thr[NH];
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
-        m_ref[i] = -INFINITY;                                 // no key seen yet
-        nmr[i] = 0.0f;                                        // -(m_ref if finite, else 0)
-        l_run[i] = 0.0f;
-        thr[i] = -INFINITY;                                   // -inf until the row has a reference, then tau
-    }
-    f32x16_t o[NT32];                                         // O^T, columns [32 v, 32 v + 32) of all rows
-#pragma unroll
-    for (int r = 0; r < NT32; ++r)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[r][e] = 0.0f;
-
-    f32x4_t zs[NH];                                           // scores of the previous step, relative to m
-    f16x2_t vsh[2];                                           // V scales of the previous step's keys (fp16 pairs)
-    f16x2_t vmax2 = {(_Float16)0.0f, (_Float16)0.0f};         // largest V scales of any key this lane scored
-#pragma unroll
-    for (int i = 0; i < NH; ++i) zs[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) vsh[j] = f16x2_t{(_Float16)0.0f, (_Float16)0.0f};
-    const float zscale = a.sm_scale * kLog2e;
-    float* const red = reinterpret_cast<float*>(lds + C::M_OFF);
-    float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
-    int id_next = h == 0 ? clamp_page(idj[kKAhead]) : clamp_page(idj[1]);   // K (half 0) or V page of the next copies
-    int id_v = clamp_page(idj[1]);                                          // half 0's V page of the next copies
-
-    for (int it = 0; it < n + 2; ++it) {
-        // this wave's copies of K(it) or V(it - 2) (position it - 3) have landed:
-        // at most the copies of positions it - 2 and it - 1 are in flight.  The
-        // barrier publishes them, the flags of step it - 1 and the P' tiles of
-        // step it - 2.
-        if (h == 0) {
-            if (it >= 2) wait_vmcnt<2 * (KC_STEP + NV0)>();
-            else if (it == 1) wait_vmcnt<KC_START + KC_STEP + 2 * NV0>();
-            else wait_vmcnt<2 * KC_START + NV0>();
-        } else {
-            if (it >= 1) wait_vmcnt<2 * NV1>();
-            else wait_vmcnt<NV1>();
+        for (int i = 0; i < NH; ++i) {
+            m_ref[i] = -INFINITY;                             // no key seen yet
+            nmr[i] = 0.0f;                                    // -(m_ref if finite, else 0)
+            l_run[i] = 0.0f;
+            thr[i] = -INFINITY;                               // -inf until the row has a reference, then tau
         }
-        lds_barrier();
-        const bool do_sm = it >= 1 && it <= n;
-        u32x2_t fl = u32x2_t{0u, 0u};
-        if (do_sm) fl = *reinterpret_cast<const u32x2_t*>(lds + C::F_OFF + ((it - 1) & 1) * kWaves);
-        // ---- copies for later steps
-        if (h == 0) {
-            issue_k(it + kKAhead, id_next);
-            issue_v(it + 1, id_v, 0, NV0);
-            // a page id past this wave's pages is read from the split's first
-            // entry, which always exists
-            if (lane == 0)
-                dma4_to_lds(it + kIdAhead <= last_valid ? bt + 4 * (it + kIdAhead) : bt - w,
-                            lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + w) * 4);
-        } else {
-            issue_v(it + 1, id_next, NV0, NI);
+        f32x4_t zs[2][NH];                                    // scores of the previous step, relative to m
+        f16x2_t vsh[2][2];                                    // V scales of the previous step's keys (fp16 pairs)
+        f16x2_t vmax2 = {(_Float16)0.0f, (_Float16)0.0f};     // largest V scales of any key this lane scored
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+            for (int i = 0; i < NH; ++i) zs[k][i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) vsh[k][j] = f16x2_t{(_Float16)0.0f, (_Float16)0.0f};
         }
+        const float zscale = a.sm_scale * kLog2e;
 
-        // ---- P V of step it - 2: O^T += V^T P'^T for this wave's 32 columns
-        if (it >= 2 && v < C::PVW) {
-            const int pstep = it - 2;
-            const uint8_t* vst = lds + C::V_OFF + (pstep & (kRing - 1)) * C::SLOT + (lane >> 5) * (D * 8) +
-                                 (32 * v + (lane & 31)) * 8;
-            const uint8_t* pbr = lds + C::P_OFF + (pstep & 1) * C::PBUF + lane * 16;
-#pragma unroll
-            for (int p = 0; p < kPagesPerIter; ++p) {
-                f16x8_t pf[NT32];
-#pragma unroll
-                for (int r = 0; r < NT32; ++r) pf[r] = *reinterpret_cast<const f16x8_t*>(pbr + (p * NT32 + r) * 1024);
-                const f16x8_t vf = codes8_to_f16(*reinterpret_cast<const u32x2_t*>(vst + p * C::PAGE));
-#pragma unroll
-                for (int r = 0; r < NT32; ++r)
-                    o[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[r], o[r], 0, 0, 0);
-            }
-        }
-
-        // ---- references.  A wave's flag says some score of its tiles and page
-        // exceeded the row's reference by more than the page's slack (bit 0), and
-        // whether a V scale of the page exceeds 255 (bit 1).  Without bit 0
-        // anywhere no reference moves: every p <= 2^slack of its page and P'
-        // stays inside fp16.  Otherwise the exact step maxima are exchanged, the
-        // rows beyond the step's slack move to them and O is rescaled.
-        uint32_t flags = __builtin_amdgcn_readfirstlane(fl[0] | fl[1]);
-        flags |= flags >> 16;
-        flags = (flags | (flags >> 8)) & 3u;
-        if (flags & 1u) {                                     // rare after the first step
-            const float tau = (flags & 2u) ? 0.0f : kTau;
-#pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const float mx = group4_max(fmaxf(fmaxf(zs[i][0], zs[i][1]), fmaxf(zs[i][2], zs[i][3])));
-                if (gq == 0) red[(16 * (t0 + i) + li) * kPagesPerIter + w] = it - 1 <= last_valid ? mx : -INFINITY;
-            }
+        for (int it = 0; it < n + 2; ++it) {
+            // the K pages of step it, the flags of step it - 1 and (for the
+            // output waves) the P' tiles of step it - 2 are published
             lds_barrier();
-            bool moved = false;
+            const bool do_sm = it >= 1 && it <= n;
+            const uint32_t flags = do_sm ? read_flags(it - 1) : 0u;
+            // ---- references.  A flag says some score of the wave's pages
+            // exceeded the row's reference by more than the slack (bit 0), and
+            // whether a V scale of them exceeds 255 (bit 1).  Without bit 0
+            // anywhere no reference moves: every p <= 2^slack and P' stays inside
+            // fp16.  Otherwise the exact step maxima are exchanged, the rows
+            // beyond the step's slack move to them and the output waves rescale O.
+            if (flags & 1u) {                                 // rare after the first step
+                const float tau = (flags & 2u) ? 0.0f : kTau;
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const f32x4_t mw = *reinterpret_cast<const f32x4_t*>(red + (16 * (t0 + i) + li) * kPagesPerIter);
-                const float mstep = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-                const bool fresh = m_ref[i] == -INFINITY;
-                const bool move = fresh ? mstep > -INFINITY : mstep > tau;
-                float alpha = 1.0f;
-                if (move) {
-                    alpha = fresh ? 0.0f : __builtin_amdgcn_exp2f(-mstep);
-                    m_ref[i] = (fresh ? 0.0f : m_ref[i]) + mstep;
-                    nmr[i] = -m_ref[i];
-                    thr[i] = kTau;
-                    l_run[i] *= alpha;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) zs[i][j] -= mstep;
+                for (int i = 0; i < NH; ++i) {
+                    const f32x4_t z0 = zs[0][i], z1 = zs[1][i];
+                    const float m4 = fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
+                                           fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3])));
+                    const float mx = group4_max(m4);
+                    if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = mx;
                 }
-                if (w == 0 && gq == 0) rowv[16 * (t0 + i) + li] = alpha;
-                moved |= __builtin_amdgcn_ballot_w64(move) != 0;
+                lds_barrier();
+#pragma unroll
+                for (int i = 0; i < NH; ++i) {
+                    const u32x2_t mw = *reinterpret_cast<const u32x2_t*>(red + (16 * (t0 + i) + li) * 2);
+                    const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));
+                    const bool fresh = m_ref[i] == -INFINITY;
+                    const bool move = fresh ? mstep > -INFINITY : mstep > tau;
+                    float alpha = 1.0f;
+                    if (move) {
+                        alpha = fresh ? 0.0f : __builtin_amdgcn_exp2f(-mstep);
+                        m_ref[i] = (fresh ? 0.0f : m_ref[i]) + mstep;
+                        nmr[i] = -m_ref[i];
+                        thr[i] = kTau;
+                        l_run[i] *= alpha;
+#pragma unroll
+                        for (int k = 0; k < 2; ++k)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) zs[k][i][j] -= mstep;
+                    }
+                    if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = alpha;
+                }
+                lds_barrier();                                // factors written, maxima read
             }
-            lds_barrier();                                    // factors written, maxima read
-            // O holds P V up to step it - 2, made with the old references
-            if (v < C::PVW) {
+            if (it == 1) {                                    // first references (O is still zero)
 #pragma unroll
-                for (int r = 0; r < NT32; ++r) {
-                    const int row = 32 * r + (lane & 31);
-                    const float al = row < 2 * NH * 16 ? rowv[row] : 1.0f;
+                for (int i = 0; i < NH; ++i) {
+                    const u32x2_t mw = *reinterpret_cast<const u32x2_t*>(red + (16 * (t0 + i) + li) * 2);
+                    const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));
+                    if (mstep > -INFINITY) {
+                        m_ref[i] = mstep;
+                        nmr[i] = -mstep;
+                        thr[i] = kTau;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) o[r][e] *= al;
+                        for (int k = 0; k < 2; ++k)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) zs[k][i][j] -= mstep;
+                    }
                 }
             }
-            (void)moved;
-        }
 
-        // ---- softmax of step it - 1: p = exp2(z - m), P' = p * s_v, tile by tile.
-        // A wave without a page in that step left z = -inf: its P' tiles are zero,
-        // so P V runs over every page of a step without a branch.
-        if (do_sm) {
-            _Float16* pb = reinterpret_cast<_Float16*>(lds + C::P_OFF + ((it - 1) & 1) * C::PBUF);
+            // ---- softmax of step it - 1: p = exp2(z - m), P' = p * s_v, tile by
+            // tile.  A page the split lacks left z = -inf: its P' tiles are zero,
+            // so P V runs over every page of a step without a branch.
+            auto softmax_page = [&](int k) {
+                _Float16* pb = reinterpret_cast<_Float16*>(lds + C::P_OFF + ((it - 1) & 1) * C::PBUF);
+                const int p = 2 * pp + k;
 #pragma unroll
-            for (int i = 0; i < NH; ++i) {
-                const int t = t0 + i;
-                float p[4];
+                for (int i = 0; i < NH; ++i) {
+                    const int t = t0 + i;
+                    float e[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(zs[i][j]);     // exp2(-inf) = 0
-                // p rounded once to fp16; the row sum adds exactly these values
-                const f16x2_t h0 = {(_Float16)p[0], (_Float16)p[1]}, h1 = {(_Float16)p[2], (_Float16)p[3]};
-                const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-                l_run[i] = __builtin_amdgcn_fdot2(h0, one2, l_run[i], false);
-                l_run[i] = __builtin_amdgcn_fdot2(h1, one2, l_run[i], false);
-                u32x2_t packed;
-                packed[0] = bit_cast<uint32_t>(h0 * vsh[0]);
-                packed[1] = bit_cast<uint32_t>(h1 * vsh[1]);
-                // reader lane of the 32-row tile t/2: rows 16 (t&1) + li, keys 8 (gq>>1) + 4 (gq&1) + j
-                *reinterpret_cast<u32x2_t*>(pb + ((w * NT32 + (t >> 1)) * 64 + 32 * (gq >> 1) + 16 * (t & 1) + li) * 8 +
-                                            4 * (gq & 1)) = packed;
-            }
-        }
-
-        // ---- Q K^T of step it for page w and this half's tiles
-        if (it < n) {
-            uint32_t flag = 0;
-            if (it <= last_valid) {
-                const int slot = it & (kRing - 1);
-                const uint8_t* kpage = lds + C::K_OFF + slot * C::SLOT + w * C::PAGE + li * D;
+                    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(zs[k][i][j]);   // exp2(-inf) = 0
+                    // p rounded once to fp16; the row sum adds exactly these values
+                    const f16x2_t h0 = {(_Float16)e[0], (_Float16)e[1]}, h1 = {(_Float16)e[2], (_Float16)e[3]};
+                    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+                    l_run[i] = __builtin_amdgcn_fdot2(h0, one2, l_run[i], false);
+                    l_run[i] = __builtin_amdgcn_fdot2(h1, one2, l_run[i], false);
+                    u32x2_t packed;
+                    packed[0] = bit_cast<uint32_t>(h0 * vsh[k][0]);
+                    packed[1] = bit_cast<uint32_t>(h1 * vsh[k][1]);
+                    // reader lane of the 32-row tile t/2: rows 16 (t&1) + li, keys 8 (gq>>1) + 4 (gq&1) + j
+                    *reinterpret_cast<u32x2_t*>(pb + ((p * NT32 + (t >> 1)) * 64 + 32 * (gq >> 1) + 16 * (t & 1) + li) * 8 +
+                                                4 * (gq & 1)) = packed;
+                }
+            };
+            // ---- Q K^T of step it, page 2 pp + k: K rows of the page from LDS
+            // (lane (gq, li) reads chunks 4 cc + gq of key row li), then the
+            // scores z = (q . (1152 + x) - 1152 sum q) * s_k * scale * log2(e) - m
+            const int slot = it & (kRing - 1);
+            auto read_k = [&](int k, u32x4_t (&kraw)[KB / 2], u32x2_t& ks, u32x2_t& vs) {
+                const int p = 2 * pp + k;
+                const uint8_t* kpage = lds + C::K_OFF + slot * C::SLOT + p * C::PAGE + li * D;
                 const int swz = k_swizzle<D>(li);
-                u32x4_t kraw[KB / 2];
 #pragma unroll
-                for (int c = 0; c < KB / 2; ++c)
-                    kraw[c] = *reinterpret_cast<const u32x4_t*>(kpage + 16 * ((4 * c + gq) ^ swz));
-                // lane (gq, li) holds keys 4 gq + j of the page, row 16 (t0 + i) + li
-                const uint8_t* sc = lds + C::S_OFF + slot * C::SSLOT + w * 64;
-                const u32x2_t ks = *reinterpret_cast<const u32x2_t*>(sc + 8 * gq);
-                const u32x2_t vs = *reinterpret_cast<const u32x2_t*>(sc + 32 + 8 * gq);
-                f32x4_t acc[NH];
+                for (int cc = 0; cc < KB / 2; ++cc)
+                    kraw[cc] = *reinterpret_cast<const u32x4_t*>(kpage + 16 * ((4 * cc + gq) ^ swz));
+                const uint8_t* sc = lds + C::S_OFF + slot * C::SSLOT + p * 64;
+                ks = *reinterpret_cast<const u32x2_t*>(sc + 8 * gq);
+                vs = *reinterpret_cast<const u32x2_t*>(sc + 32 + 8 * gq);
+            };
+            auto qk_chunk = [&](const u32x4_t kr, int cc, f32x4_t (&acc)[NH]) {
+                f16x8_t k0, k1;
+                codes16_to_f16_biased(kr, k0, k1);
 #pragma unroll
-                for (int i = 0; i < NH; ++i) acc[i] = nqb[i];
+                for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * cc][i], acc[i], 0, 0, 0);
 #pragma unroll
-                for (int c = 0; c < KB / 2; ++c) {
-                    f16x8_t k0, k1;
-                    codes16_to_f16_biased(kraw[c], k0, k1);
-#pragma unroll
-                    for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * c][i], acc[i], 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * c + 1][i], acc[i], 0, 0, 0);
-                }
+                for (int i = 0; i < NH; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * cc + 1][i], acc[i], 0, 0, 0);
+            };
+            // lane (gq, li) holds keys 4 gq + j of the page, row 16 (t0 + i) + li;
+            // returns whether a score exceeded its row's threshold
+            auto finish_page = [&](int k, const f32x4_t (&acc)[NH], const u32x2_t ks, const u32x2_t vs,
+                                   const bool may_mask, bool& big) -> bool {
+                const int p = 2 * pp + k;
                 float kc[4];
                 kc[0] = f16lo(ks[0]) * zscale;
                 kc[1] = f16hi(ks[0]) * zscale;
                 kc[2] = f16lo(ks[1]) * zscale;
                 kc[3] = f16hi(ks[1]) * zscale;
-                vsh[0] = bit_cast<f16x2_t>(vs[0]);
-                vsh[1] = bit_cast<f16x2_t>(vs[1]);
-                const int key0 = (pg_begin + kPagesPerIter * it + w) * kPage;
+                vsh[k][0] = bit_cast<f16x2_t>(vs[0]);
+                vsh[k][1] = bit_cast<f16x2_t>(vs[1]);
+                const int key0 = (pg_begin + kPagesPerIter * it + p) * kPage;
                 // every key of the page is visible to every row (padded rows see q = 0)
-                const bool masked = !(key0 + kPage - 1 <= ctx - dl);
+                const bool masked = may_mask && !(key0 + kPage - 1 <= ctx - dl);
                 const int kl = key0 + 4 * gq;
                 if (masked) {                                 // keys past the context carry no V weight
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const uint32_t keep = (kl + 2 * j < ctx ? 0xffffu : 0u) | (kl + 2 * j + 1 < ctx ? 0xffff0000u : 0u);
-                        vsh[j] = bit_cast<f16x2_t>(bit_cast<uint32_t>(vsh[j]) & keep);
+                        vsh[k][j] = bit_cast<f16x2_t>(bit_cast<uint32_t>(vsh[k][j]) & keep);
                     }
                 }
-                // a V scale above 255 leaves no fp16 room above p = 1: slack 0 for this page
-                const f16x2_t vm2 = __builtin_elementwise_max(vsh[0], vsh[1]);
+                // a V scale above 255 leaves no fp16 room above p = 1: slack 0 for the step
+                const f16x2_t vm2 = __builtin_elementwise_max(vsh[k][0], vsh[k][1]);
                 vmax2 = __builtin_elementwise_max(vmax2, vm2);
                 const float vmx = fmaxf((float)vm2[0], (float)vm2[1]);
-                const bool big = __builtin_amdgcn_ballot_w64(vmx > 255.0f) != 0;
+                const bool bigk = __builtin_amdgcn_ballot_w64(vmx > 255.0f) != 0;
+                big |= bigk;
                 bool exceed = false;
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) zs[i][j] = __builtin_fmaf(acc[i][j], kc[j], nmr[i]);
+                    for (int j = 0; j < 4; ++j) zs[k][i][j] = __builtin_fmaf(acc[i][j], kc[j], nmr[i]);
                     if (masked) {
                         const int row = 16 * (t0 + i) + li;   // last key the row may see; -1: padded row
                         const int last_key = row < rows ? ctx - dl + row / G : -1;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) zs[i][j] = kl + j <= last_key ? zs[i][j] : -INFINITY;
+                        for (int j = 0; j < 4; ++j) zs[k][i][j] = kl + j <= last_key ? zs[k][i][j] : -INFINITY;
                     }
-                    const float mx = fmaxf(fmaxf(zs[i][0], zs[i][1]), fmaxf(zs[i][2], zs[i][3]));
-                    exceed |= mx > (big ? fminf(thr[i], 0.0f) : thr[i]);
+                    const float mx = fmaxf(fmaxf(zs[k][i][0], zs[k][i][1]), fmaxf(zs[k][i][2], zs[k][i][3]));
+                    exceed |= mx > (bigk ? fminf(thr[i], 0.0f) : thr[i]);
                 }
-                flag = (__builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u) | (big ? 2u : 0u);
+                return exceed;
+            };
+            auto write_flag = [&](bool exceed, bool big) {
+                const uint32_t flag = (__builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u) | (big ? 2u : 0u);
+                if (lane == 0)
+                    *reinterpret_cast<uint8_t*>(lds + C::F_OFF + (it & 1) * kWaves + v) = (uint8_t)flag;
+            };
+
+            // Steady steps (both pages present, no key past any row's view) run
+            // as one block: the K reads go first, so their latency overlaps the
+            // softmax, and the two pages' MFMA chains interleave.
+            const int key_end = (pg_begin + kPagesPerIter * it + 2 * pp + 2) * kPage;   // one past page 2 pp + 1
+            if (do_sm && it < n && it <= lv1 && key_end - 1 <= ctx - dl) {
+                u32x4_t kraw[2][KB / 2];
+                u32x2_t ks[2], vs[2];
+                read_k(0, kraw[0], ks[0], vs[0]);
+                read_k(1, kraw[1], ks[1], vs[1]);
+                softmax_page(0);
+                softmax_page(1);
+                f32x4_t acc[2][NH];
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                    for (int i = 0; i < NH; ++i) acc[k][i] = nqb[i];
+#pragma unroll
+                for (int cc = 0; cc < KB / 2; ++cc) {
+                    qk_chunk(kraw[0][cc], cc, acc[0]);
+                    qk_chunk(kraw[1][cc], cc, acc[1]);
+                }
+                bool big = false;
+                const bool e0 = finish_page(0, acc[0], ks[0], vs[0], false, big);
+                const bool e1 = finish_page(1, acc[1], ks[1], vs[1], false, big);
+                write_flag(e0 || e1, big);
             } else {
+                if (do_sm) {
+                    softmax_page(0);
+                    softmax_page(1);
+                }
+                if (it < n) {
+                    bool exceed = false, big = false;
 #pragma unroll
-                for (int i = 0; i < NH; ++i) zs[i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                    for (int k = 0; k < 2; ++k) {
+                        if (it <= (k == 0 ? lv0 : lv1)) {
+                            u32x4_t kraw[KB / 2];
+                            u32x2_t ks, vs;
+                            read_k(k, kraw, ks, vs);
+                            f32x4_t acc[NH];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) vsh[j] = f16x2_t{(_Float16)0.0f, (_Float16)0.0f};
+                            for (int i = 0; i < NH; ++i) acc[i] = nqb[i];
+#pragma unroll
+                            for (int cc = 0; cc < KB / 2; ++cc) qk_chunk(kraw[cc], cc, acc);
+                            exceed |= finish_page(k, acc, ks, vs, true, big);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < NH; ++i) zs[k][i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) vsh[k][j] = f16x2_t{(_Float16)0.0f, (_Float16)0.0f};
+                        }
+                    }
+                    if (it == 0) {
+                        // the first references are the exact maxima of step 0,
+                        // set at step 1 after the barrier: no flag, no exchange
+#pragma unroll
+                        for (int i = 0; i < NH; ++i) {
+                            const f32x4_t z0 = zs[0][i], z1 = zs[1][i];
+                            const float m4 = fmaxf(fmaxf(fmaxf(z0[0], z0[1]), fmaxf(z0[2], z0[3])),
+                                                   fmaxf(fmaxf(z1[0], z1[1]), fmaxf(z1[2], z1[3])));
+                            const float mx = group4_max(m4);
+                            if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = mx;
+                        }
+                        exceed = false;
+                    }
+                    write_flag(exceed, big);
+                }
             }
-            if (lane == 0)
-                *reinterpret_cast<uint8_t*>(lds + C::F_OFF + (it & 1) * kWaves + v) = (uint8_t)flag;
         }
-        // page id of this wave's next copy: its ring entry was copied at least
-        // three steps ago, so the wait at the top of this step covered it
-        id_next = clamp_page(ring_id(h == 0 ? it + 1 + kKAhead : it + 2));
-        if (h == 0) id_v = clamp_page(ring_id(it + 2));
+
+        // ---- epilogue, score side: row sums across lane groups, the references
+        // and the largest V scale
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const float l = group4_sum(l_run[i]);
+            if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = l;
+            if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = m_ref[i];
+        }
+        if (a.out == nullptr) {
+            const float vm = wave_max(fmaxf((float)vmax2[0], (float)vmax2[1]));
+            if (lane == 0) vtop[v] = vm;
+        }
+        lds_barrier();
+        return;
+    }
+
+    // ================= output waves =================
+    const bool owns = c * SPW < C::NSL;                       // D = 64: two waves own the columns
+    f32x16_t o[SPW][NT32];                                    // O^T, columns [32 (c SPW + sl), +32) of all rows
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int r = 0; r < NT32; ++r)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[sl][r][e] = 0.0f;
+    int id_k = clamp_page(idj[kKAhead]);                      // K page of the next copies
+    int id_v = clamp_page(idj[1]);                            // V page of the next copies
+
+    for (int it = 0; it < n + 2; ++it) {
+        // this wave's copies of K(it) and V(it - 2) (position it - 3) have
+        // landed: at most the copies of positions it - 2 and it - 1 are in flight
+        if (it >= 2) wait_vmcnt<2 * (KC_STEP + NI)>();
+        else if (it == 1) wait_vmcnt<KC_START + KC_STEP + 2 * NI>();
+        else wait_vmcnt<2 * KC_START + NI>();
+        lds_barrier();
+        const bool do_sm = it >= 1 && it <= n;
+        const uint32_t flags = do_sm ? read_flags(it - 1) : 0u;
+        // ---- copies for later steps; a page id past the split's pages is read
+        // from the split's first entry of page c's column, which always exists
+        issue_k(it + kKAhead, id_k);
+        issue_v(it + 1, id_v);
+        if (lane == 0)
+            dma4_to_lds(it + kIdAhead <= last_c ? bt + 4 * (it + kIdAhead) : bt - c,
+                        lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + c) * 4);
+
+        // ---- P V of step it - 2: O^T += V^T P'^T for this wave's columns.
+        // Every operand is read first, so the LDS round trips overlap.
+        if (it >= 2 && owns) {
+            const int pstep = it - 2;
+            const uint8_t* vst = lds + C::V_OFF + (pstep & (kRing - 1)) * C::SLOT + (lane >> 5) * (D * 8) +
+                                 (32 * c * SPW + (lane & 31)) * 8;
+            const uint8_t* pbr = lds + C::P_OFF + (pstep & 1) * C::PBUF + lane * 16;
+            f16x8_t pf[kPagesPerIter][NT32];
+            u32x2_t vr[kPagesPerIter][SPW];
+#pragma unroll
+            for (int p = 0; p < kPagesPerIter; ++p) {
+#pragma unroll
+                for (int sl = 0; sl < SPW; ++sl) vr[p][sl] = *reinterpret_cast<const u32x2_t*>(vst + p * C::PAGE + 256 * sl);
+#pragma unroll
+                for (int r = 0; r < NT32; ++r) pf[p][r] = *reinterpret_cast<const f16x8_t*>(pbr + (p * NT32 + r) * 1024);
+            }
+#pragma unroll
+            for (int p = 0; p < kPagesPerIter; ++p) {
+#pragma unroll
+                for (int sl = 0; sl < SPW; ++sl) {
+                    const f16x8_t vf = codes8_to_f16(vr[p][sl]);
+#pragma unroll
+                    for (int r = 0; r < NT32; ++r)
+                        o[sl][r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[p][r], o[sl][r], 0, 0, 0);
+                }
+            }
+        }
+
+        if (flags & 1u) {                                     // the score waves move references
+            lds_barrier();
+            lds_barrier();                                    // factors written
+            // O holds P V up to step it - 2, made with the old references
+            if (owns) {
+#pragma unroll
+                for (int r = 0; r < NT32; ++r) {
+                    const int row = 32 * r + (lane & 31);
+                    const float al = row < 2 * NH * 16 ? rowv[row] : 1.0f;
+#pragma unroll
+                    for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) o[sl][r][e] *= al;
+                }
+            }
+        }
+        // page ids of this wave's next copies: their ring entries were copied at
+        // least three steps ago, so the wait at the top of this step covered them
+        id_k = clamp_page(ring_id(it + 1 + kKAhead));
+        id_v = clamp_page(ring_id(it + 2));
     }
 
     wait_vmcnt<0>();                                          // the lane-0 copies past the pages
-    // ---- epilogue: row sums across lane groups and pages, then normalise
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
-        const float l = group4_sum(l_run[i]);
-        if (gq == 0) red[(16 * (t0 + i) + li) * kPagesPerIter + w] = l;
-        if (w == 0 && gq == 0) rowv[16 * (t0 + i) + li] = m_ref[i];
-    }
-    float* const vtop = reinterpret_cast<float*>(lds + C::F_OFF);   // the flags are spent by now
+    lds_barrier();                                            // row sums, references, V scale maxima
+    if (!owns) return;
+    // ---- epilogue, output side.  fp16 partials are scaled by 2^-k, k from the
+    // largest V scale of the split, so that |o| <= 127 * that scale * 2^-k stays
+    // inside binary16; k goes into the log-sum-exp, which leaves e^lse * o unchanged
+    int kshift = 0;
     if (a.out == nullptr) {
-        const float vm = wave_max(fmaxf((float)vmax2[0], (float)vmax2[1]));
-        if (lane == 0) vtop[v] = vm;
+        float vm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vm = fmaxf(vm, vtop[i]);
+        const float bound = 127.0f * vm;
+        // floor(log2 bound) from the binary32 exponent field (bound is normal here)
+        const int e2 = (int)((bit_cast<uint32_t>(bound) >> 23) & 0xffu) - 127;
+        kshift = bound < 32768.0f ? 0 : max(0, e2 + 1 - 15);
     }
-    lds_barrier();
-    if (v < C::PVW) {
-        // fp16 partials are scaled by 2^-k, k from the largest V scale of the
-        // split, so that |o| <= 127 * that scale * 2^-k stays inside binary16;
-        // k goes into the log-sum-exp, which leaves e^lse * o unchanged
-        int kshift = 0;
-        if (a.out == nullptr) {
-            float vm = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kWaves; ++i) vm = fmaxf(vm, vtop[i]);
-            const float bound = 127.0f * vm;
-            // floor(log2 bound) from the binary32 exponent field (bound is normal here)
-            const int e2 = (int)((bit_cast<uint32_t>(bound) >> 23) & 0xffu) - 127;
-            kshift = bound < 32768.0f ? 0 : max(0, e2 + 1 - 15);
-        }
+    for (int r = 0; r < NT32; ++r) {
+        const int row = 32 * r + (lane & 31);
+        if (row >= rows) continue;
+        const u32x2_t lw = *reinterpret_cast<const u32x2_t*>(red + row * 2);
+        const float l = bit_cast<float>(lw[0]) + bit_cast<float>(lw[1]);
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const int t = row / G, hq = g * G + row % G;
 #pragma unroll
-        for (int r = 0; r < NT32; ++r) {
-            const int row = 32 * r + (lane & 31);
-            if (row >= rows) continue;
-            const f32x4_t lw = *reinterpret_cast<const f32x4_t*>(red + row * kPagesPerIter);
-            const float l = (lw[0] + lw[1]) + (lw[2] + lw[3]);
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            const int t = row / G, hq = g * G + row % G;
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int vs = c * SPW + sl;                      // 32-column slice
             if (a.out != nullptr) {
                 uint16_t* orow = a.out + (((size_t)b * a.T_max + t) * Hq + hq) * D;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d = 32 * v + 8 * q4 + 4 * (lane >> 5);
+                    const int d = 32 * vs + 8 * q4 + 4 * (lane >> 5);
                     u32x2_t x;
-                    x[0] = (uint32_t)f32_to_bf16_rne(o[r][4 * q4] * inv) |
-                           ((uint32_t)f32_to_bf16_rne(o[r][4 * q4 + 1] * inv) << 16);
-                    x[1] = (uint32_t)f32_to_bf16_rne(o[r][4 * q4 + 2] * inv) |
-                           ((uint32_t)f32_to_bf16_rne(o[r][4 * q4 + 3] * inv) << 16);
+                    x[0] = (uint32_t)f32_to_bf16_rne(o[sl][r][4 * q4] * inv) |
+                           ((uint32_t)f32_to_bf16_rne(o[sl][r][4 * q4 + 1] * inv) << 16);
+                    x[1] = (uint32_t)f32_to_bf16_rne(o[sl][r][4 * q4 + 2] * inv) |
+                           ((uint32_t)f32_to_bf16_rne(o[sl][r][4 * q4 + 3] * inv) << 16);
                     *reinterpret_cast<u32x2_t*>(orow + d) = x;
                 }
             } else {
-                // tile order [slice v][32-row tile r][q4][lane][4]: every store of
+                // tile order [slice][32-row tile r][q4][lane][4]: every store of
                 // the wave writes 512 contiguous bytes
                 const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
-                uint16_t* dst = a.part_h + blk * (16 * G * D) + (size_t)(((v * C::NT32 + r) * 4) * 64 + lane) * 4;
+                uint16_t* dst = a.part_h + blk * (16 * G * D) + (size_t)(((vs * C::NT32 + r) * 4) * 64 + lane) * 4;
                 const float sc = __builtin_ldexpf(inv, -kshift);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     u32x2_t x;
-                    x[0] = pack_f16x2(o[r][4 * q4] * sc, o[r][4 * q4 + 1] * sc);
-                    x[1] = pack_f16x2(o[r][4 * q4 + 2] * sc, o[r][4 * q4 + 3] * sc);
+                    x[0] = pack_f16x2(o[sl][r][4 * q4] * sc, o[sl][r][4 * q4 + 1] * sc);
+                    x[1] = pack_f16x2(o[sl][r][4 * q4 + 2] * sc, o[sl][r][4 * q4 + 3] * sc);
                     *reinterpret_cast<u32x2_t*>(dst + q4 * 256) = x;
                 }
-                if (v == 0 && lane < 32) {
-                    const float m = rowv[row];
-                    a.part_hlse[blk * (16 * G) + row] =
-                        l > 0.0f ? (m + __builtin_log2f(l) + (float)kshift) * kLn2 : -INFINITY;
-                }
             }
+        }
+        if (a.out == nullptr && c == 0 && lane < 32) {
+            const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
+            const float m = rowv[row];
+            a.part_hlse[blk * (16 * G) + row] = l > 0.0f ? (m + __builtin_log2f(l) + (float)kshift) * kLn2 : -INFINITY;
         }
     }
 }
