@@ -53,6 +53,7 @@ def _declare(lib):
                                                  _I, _I, _I, _I, _I, _I, _I, _D, _I, _I,
                                                  _P, _P]
     lib.splash_ref_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I]
+    lib.splash_ref_verify_accept.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I]
     lib.splash_ref_num_threads.argtypes = []
     lib.splash_ref_num_threads.restype = ctypes.c_int
     lib.ref_quantize_row.argtypes = [_P, _I, _P, _P]
@@ -62,7 +63,7 @@ def _declare(lib):
     lib.ref_f16_to_f32.argtypes = [ctypes.c_uint16]
     lib.ref_f16_to_f32.restype = ctypes.c_float
     for f in ("splash_ref_kv_append_int8", "splash_ref_verify_attn", "splash_ref_verify_attn_rows",
-              "splash_ref_verify_attn_split", "splash_ref_splitk_merge"):
+              "splash_ref_verify_attn_split", "splash_ref_splitk_merge", "splash_ref_verify_accept"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -116,6 +117,22 @@ class Oracle:
             self._ptr(context_lens), self._ptr(draft_lens), B, T_max, Hkv, D, P, num_pages)
         if rc:
             raise ValueError(f"oracle append rejected its arguments (rc={rc})")
+
+    def verify_accept(self, logits, block_tokens, draft_lens, context_lens):
+        """logits: bf16 bits uint16 [B][T_max][V]; block_tokens int32 [B][T_max].
+        Returns (accepted int32 [B], next_token int32 [B], new context_lens int32 [B])."""
+        logits = np.ascontiguousarray(logits, dtype=np.uint16)
+        B, T_max, V = logits.shape
+        blk = np.ascontiguousarray(block_tokens, dtype=np.int32)
+        dl = np.ascontiguousarray(draft_lens, dtype=np.int32)
+        ctx = np.array(context_lens, dtype=np.int32, copy=True)
+        acc = np.empty(B, dtype=np.int32)
+        nxt = np.empty(B, dtype=np.int32)
+        rc = self.lib.splash_ref_verify_accept(self._ptr(logits), self._ptr(blk), self._ptr(dl), self._ptr(ctx),
+                                               self._ptr(acc), self._ptr(nxt), B, T_max, V)
+        if rc:
+            raise ValueError(f"oracle verify_accept rejected its arguments (rc={rc})")
+        return acc, nxt, ctx
 
     def verify_attn(self, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                     draft_lens, Hkv, sm_scale, out=None):

@@ -463,3 +463,59 @@ int splash_ref_splitk_merge(const float* part_o, const float* part_lse, double* 
             }
     return REF_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * Acceptance of a verified draft block (discuss.pytorch.kr summary, section
+ * "DFlash 2 speculative decoding as the default path": the draft model
+ * proposes a block, the target checks the whole block in one forward pass, the
+ * final output is identical to autoregressive decoding, and drafting,
+ * verification, acceptance and the state update run as one unit).
+ *
+ * Written as that definition: the target's greedy choice after block position
+ * t is y_t = argmax_v logits[b][t][v] (the largest value, compared as the exact
+ * value of the bf16 number; among equal values the lowest token id).  Greedy
+ * autoregressive decoding emits y_0 first; it keeps emitting the drafts for as
+ * long as each draft equals the token greedy decoding would have chosen at its
+ * position, and the first disagreement (or the end of the block) ends the
+ * step with the target's own choice at that position.  So
+ *   accepted   = 1 + number of leading i with block[i + 1] == y_i (i < d - 1)
+ *   next_token = y_{accepted - 1}
+ *   context_lens[b] -= d - accepted   (the rejected drafts leave the cache)
+ * d = draft_lens[b] = 0 is a no-op: accepted = 0, next_token = -1.
+ * logits: bf16 bits [B][T_max][V]; rows t >= d are not read.
+ * ------------------------------------------------------------------------ */
+static int ref_argmax_bf16(const uint16_t* row, int V)
+{
+    int best = 0;
+    float bv = bf16_to_f32(row[0]);
+    for (int v = 1; v < V; ++v) {
+        float x = bf16_to_f32(row[v]);
+        if (x > bv) { bv = x; best = v; }          /* strictly larger: ties keep the lowest id */
+    }
+    return best;
+}
+
+int splash_ref_verify_accept(const uint16_t* logits, const int32_t* block_tokens,
+                             const int32_t* draft_lens, int32_t* context_lens,
+                             int32_t* accepted, int32_t* next_token,
+                             int B, int T_max, int V)
+{
+    if (!logits || !block_tokens || !draft_lens || !context_lens || !accepted || !next_token ||
+        B < 0 || T_max < 0 || V <= 0) return REF_ERR_ARG;
+    for (int b = 0; b < B; ++b) {
+        int d = draft_lens[b];
+        if (d < 0 || d > T_max) return REF_ERR_ARG;
+        if (d == 0) { accepted[b] = 0; next_token[b] = -1; continue; }
+        const int32_t* blk = block_tokens + (size_t)b * T_max;
+        int a = 1;
+        int y = ref_argmax_bf16(logits + ((size_t)b * T_max + 0) * V, V);
+        while (a < d && blk[a] == y) {             /* draft a matches the greedy token: keep it */
+            y = ref_argmax_bf16(logits + ((size_t)b * T_max + a) * V, V);
+            ++a;
+        }
+        accepted[b] = a;
+        next_token[b] = y;
+        context_lens[b] -= d - a;
+    }
+    return REF_OK;
+}

@@ -284,3 +284,88 @@ def make_config(cfg: int, seed: int | None = None, **over) -> Workload:
         raise ValueError(cfg)
     kw.update(over)
     return make_workload(f"config{cfg}", seed, **kw)
+
+
+# --------------------------------------------------------------------------
+# Acceptance of a verified block: synthetic target logits.  The pages name the
+# step (the target checks the drafted block in one pass and the output equals
+# autoregressive decoding) but no vocabulary; 151,936 is the vocabulary of the
+# Qwen tokenizer family the engine ships models of.  Logits are N(0, 1) * spread
+# clipped to [-32, 32], rounded to bf16; every read row gets a spike of 64.0 at a
+# drawn token, so each row's greedy token is known by construction (with
+# `ties`, a second equal spike at a higher id, so the lower id must win), and the
+# drafts copy those tokens up to a drawn acceptance point and differ there.
+# --------------------------------------------------------------------------
+VOCAB = 151936
+SPIKE = 64.0
+
+
+@dataclass
+class AcceptCase:
+    logits: np.ndarray           # bf16 bits uint16 [B][T_max][V]
+    block_tokens: np.ndarray     # int32 [B][T_max]: [last committed token, drafts...]
+    draft_lens: np.ndarray       # int32 [B]
+    context_lens: np.ndarray     # int32 [B], cache length after the block
+    planted_tokens: np.ndarray   # int32 [B][T_max]: the spike's token of each read row (-1 elsewhere)
+    planted_accept: np.ndarray   # int32 [B]: block tokens kept, by construction
+
+    @property
+    def B(self) -> int:
+        return self.logits.shape[0]
+
+    @property
+    def T_max(self) -> int:
+        return self.logits.shape[1]
+
+    @property
+    def V(self) -> int:
+        return self.logits.shape[2]
+
+
+def make_accept_case(seed: int, *, B: int, T_max: int, V: int = VOCAB, draft_lens=None, accept_lens=None,
+                     context_base: int = 4096, ties: bool = False, spread: float = 2.0) -> AcceptCase:
+    """Draw order: logits, draft lengths (if not given), planted tokens, tie tokens,
+    acceptance points (if not given), first block tokens, rejected drafts, trailing drafts."""
+    rng = np.random.default_rng(seed)
+    x = np.clip(rng.standard_normal((B, T_max, V), dtype=np.float32) * np.float32(spread), -32.0, 32.0)
+    if draft_lens is None:
+        draft_lens = rng.integers(1, T_max + 1, size=B)
+    dl = np.asarray(draft_lens, dtype=np.int32).reshape(B)
+    planted = rng.integers(0, V, size=(B, T_max)).astype(np.int32)
+    second = rng.integers(0, V, size=(B, T_max)).astype(np.int32)
+    if accept_lens is None:
+        accept_lens = np.array([rng.integers(1, d + 1) if d > 0 else 0 for d in dl])
+    acc = np.asarray(accept_lens, dtype=np.int32).reshape(B)
+    first = rng.integers(0, V, size=B).astype(np.int32)
+    wrong = rng.integers(1, V, size=(B, T_max)).astype(np.int32)
+    tail = rng.integers(0, V, size=(B, T_max)).astype(np.int32)
+    bt = np.zeros((B, T_max), dtype=np.int32)
+    for b in range(B):
+        d = int(dl[b])
+        if d == 0:
+            planted[b, :] = -1
+            continue
+        for t in range(d):
+            y = int(planted[b, t])
+            if ties and V > 1:
+                lo, hi = sorted((y, int(second[b, t])))
+                if lo == hi:
+                    hi = (lo + 1) % V
+                    lo, hi = min(lo, hi), max(lo, hi)
+                x[b, t, hi] = SPIKE
+                planted[b, t] = y = lo
+            x[b, t, y] = SPIKE
+        planted[b, d:] = -1
+        a = int(acc[b])
+        assert 1 <= a <= d, "acceptance point must lie in [1, d]"
+        bt[b, 0] = first[b]
+        for i in range(d - 1):                     # draft at block position i + 1 vs row i
+            if i < a - 1:
+                bt[b, i + 1] = planted[b, i]
+            elif i == a - 1:
+                bt[b, i + 1] = (planted[b, i] + wrong[b, i]) % V     # any token but the greedy one
+            else:
+                bt[b, i + 1] = tail[b, i]
+    ctx = np.full(B, context_base, dtype=np.int32) + dl
+    return AcceptCase(logits=_bf16_bits(x), block_tokens=bt, draft_lens=dl, context_lens=ctx,
+                      planted_tokens=planted, planted_accept=acc)

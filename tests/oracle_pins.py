@@ -20,6 +20,11 @@ pins come from the mathematics and from library routines):
   split + merge          the split path merged by the log-sum-exp identity ==
                          unsplit; merge closed forms (equal weights, one live
                          split, shift invariance)
+  acceptance             spiked logits with known greedy tokens (planted
+                         acceptance points, no block, whole block kept); ties
+                         to the lowest id, signed zeros, negatives; brute-force
+                         equality with greedy autoregressive decoding of a toy
+                         prefix-dependent target (numpy argmax)
 """
 from __future__ import annotations
 
@@ -511,6 +516,86 @@ def pin_merge_closed_forms(orc, seed=30):
     assert np.allclose(out[0], want[0], rtol=1e-6, atol=1e-7)
 
 
+# --------------------------------------------------------------------------
+# acceptance of a verified block
+# --------------------------------------------------------------------------
+def _check_planted(orc, case):
+    """Accepted length, next token and rollback against the generator's construction."""
+    acc, nxt, ctx = orc.verify_accept(case.logits, case.block_tokens, case.draft_lens, case.context_lens)
+    for b in range(case.B):
+        d, a = int(case.draft_lens[b]), int(case.planted_accept[b])
+        if d == 0:
+            assert (acc[b], nxt[b], ctx[b]) == (0, -1, case.context_lens[b]), (b, acc[b], nxt[b], ctx[b])
+            continue
+        assert acc[b] == a, f"request {b}: accepted {acc[b]}, planted {a}"
+        assert nxt[b] == case.planted_tokens[b, a - 1], f"request {b}: next {nxt[b]}"
+        assert ctx[b] == case.context_lens[b] - (d - a), f"request {b}: context {ctx[b]}"
+
+
+def pin_accept_planted(orc, seed=41):
+    """Spiked logits: each row's greedy token, and so the accepted length, is
+    known by construction (no argmax computed on the pin's side)."""
+    for i, (B, T, V) in enumerate([(6, 16, 1000), (3, 4, 64), (2, 16, 4096)]):
+        _check_planted(orc, synth.make_accept_case(seed + i, B=B, T_max=T, V=V))
+    # the edges of the acceptance point: first draft rejected, every draft kept, a one-token block
+    _check_planted(orc, synth.make_accept_case(seed + 5, B=3, T_max=16, V=500, draft_lens=[16, 16, 1],
+                                               accept_lens=[1, 16, 1]))
+    # a request with no block is a no-op
+    _check_planted(orc, synth.make_accept_case(seed + 6, B=2, T_max=8, V=300, draft_lens=[0, 5], accept_lens=[0, 5]))
+
+
+def pin_accept_ties_lowest_id(orc, seed=42):
+    """Two equal spikes per row: the lower token id is the greedy choice.  Zeros
+    of both signs are equal values; among negatives the largest value wins."""
+    _check_planted(orc, synth.make_accept_case(seed, B=6, T_max=16, V=2000, ties=True))
+    V = 64
+    lg = np.zeros((2, 1, V), np.uint16)
+    lg[0, 0, :] = 0x8000                                        # -0.0 everywhere ...
+    lg[0, 0, 5] = 0x0000                                        # ... and +0.0 at id 5
+    neg = np.full(V, -2.0, np.float32)
+    neg[37], neg[50] = -1.0, -1.5
+    lg[1, 0, :] = bf16_bits_exact(neg)
+    acc, nxt, ctx = orc.verify_accept(lg, np.zeros((2, 1), np.int32), np.array([1, 1], np.int32),
+                                      np.array([10, 10], np.int32))
+    assert list(acc) == [1, 1] and list(nxt) == [0, 37] and list(ctx) == [10, 10], (acc, nxt, ctx)
+
+
+def pin_accept_equals_greedy_decoding(orc, seed=43, V=40, n_cases=300):
+    """The output equals autoregressive decoding, by brute force: a toy target
+    whose logits depend on the whole prefix (small integers, so ties are
+    common); greedy decoding of it with numpy's argmax (first maximal id) gives
+    the reference tokens.  The tokens a step emits -- the accepted drafts, then
+    the next token -- are the first tokens greedy decoding emits, the draft
+    after them is not greedy's, and the cache keeps exactly the kept block."""
+    import zlib
+    rng = np.random.default_rng(seed)
+
+    def target(prefix):                                         # bf16 logits after `prefix`
+        key = zlib.crc32(np.asarray(prefix, np.int64).tobytes())
+        return bf16_bits_exact(np.random.default_rng(key).integers(-4, 5, size=V).astype(np.float32))
+
+    def greedy(prefix):
+        return int(np.argmax(bf16_value(target(prefix))))
+
+    for _ in range(n_cases):
+        committed = [int(t) for t in rng.integers(0, V, size=int(rng.integers(1, 6)))]
+        T = int(rng.integers(1, 9))
+        ar, pre = [], list(committed)
+        for _ in range(T):
+            ar.append(greedy(pre))
+            pre.append(ar[-1])
+        k = int(rng.integers(0, T))                             # drafts copied from greedy decoding
+        drafts = [ar[i] if i < k else int(rng.integers(0, V)) for i in range(T - 1)]
+        logits = np.stack([target(committed + drafts[:t]) for t in range(T)])
+        acc, nxt, ctx = orc.verify_accept(logits[None], np.array([[committed[-1]] + drafts], np.int32),
+                                          np.array([T], np.int32), np.array([100 + T], np.int32))
+        a = int(acc[0])
+        assert 1 <= a <= T and drafts[:a - 1] + [int(nxt[0])] == ar[:a], (committed, drafts, ar, a, nxt)
+        if a < T:
+            assert drafts[a - 1] != ar[a - 1]
+        assert int(ctx[0]) == 100 + a
+
+
 ALL_PINS = [
     pin_f16_widening_exhaustive,
     pin_f32_to_f16_matches_numpy,
@@ -532,4 +617,7 @@ ALL_PINS = [
     pin_rows_api_matches_full,
     pin_split_equals_unsplit,
     pin_merge_closed_forms,
+    pin_accept_planted,
+    pin_accept_ties_lowest_id,
+    pin_accept_equals_greedy_decoding,
 ]

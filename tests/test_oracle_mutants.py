@@ -54,6 +54,14 @@ MUTANTS = {
     "split_range_shift": ("long lo = (long)s * L * P, hi", "long lo = (long)s * L * P + 1, hi"),
     "merge_weight_sign": ("double w = exp(l - M);", "double w = exp(M - l);"),
     "merge_no_normalise": ("for (int d = 0; d < D; ++d) o[d] /= wsum;", ""),
+    # acceptance
+    "accept_ties_highest": ("if (x > bv) { bv = x; best = v; }", "if (x >= bv) { bv = x; best = v; }"),
+    "accept_compares_bits": ("float x = bf16_to_f32(row[v]);", "float x = (float)row[v];"),
+    "accept_draft_index": ("while (a < d && blk[a] == y) {", "while (a < d && blk[a - 1] == y) {"),
+    "accept_drafts_from_zero": ("int a = 1;\n        int y", "int a = 0;\n        int y"),
+    "accept_rollback_wrong": ("context_lens[b] -= d - a;", "context_lens[b] -= a;"),
+    "accept_noop_falls_through": ("if (d == 0) { accepted[b] = 0; next_token[b] = -1; continue; }",
+                                  "if (d == 0) { accepted[b] = 0; next_token[b] = -1; }"),
 }
 
 
