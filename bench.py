@@ -264,6 +264,7 @@ def main():
     # practical HBM read ceiling for the same access pattern: 4 KB pages at
     # permuted positions of a 4 GiB pool, 16-byte direct-to-LDS loads, no compute
     stream_gbs = read_ceiling_gbs(dev)
+    accept = accept_leg(dev, args.steps)
     part_bytes = verify_bytes(ctx, Hkv, D, T, Hq)
     achieved = part_bytes / (part_us * 1e-6) / 1e9
 
@@ -310,8 +311,55 @@ def main():
                      "page_read_ceiling_gbs": round(stream_gbs, 1),
                      "frac_of_page_read_ceiling": round(achieved / stream_gbs, 4)},
         "cpu_baseline": cpu,
+        "accept": accept,
     }
     print(json.dumps(line), flush=True)
+
+
+def accept_leg(dev, steps: int) -> dict:
+    """The step after verify: greedy acceptance over the target's logits (bf16,
+    151,936-token vocabulary) for the verify workloads' block shapes.  Calls go
+    back to back on logits replicas that together exceed the 256 MB Infinity
+    Cache, so the logits come from HBM; bytes are the logits of the rows read."""
+    import torch
+    import speculative_decode_attention_amd as sda
+    from speculative_decode_attention_amd import synth
+    res = {}
+    for name, B, dls in (("one_request_T16", 1, [16]), ("sixteen_requests_ragged_T16", 16, None)):
+        case = synth.make_accept_case(21, B=B, T_max=16, draft_lens=dls)
+        V = case.V
+        row_bytes = V * 2
+        R = max(2, -(-(768 << 20) // case.logits.nbytes))
+        base = torch.from_numpy(case.logits.view(np.int16)).to(dev)
+        logits = base.unsqueeze(0).repeat(R, 1, 1, 1).contiguous()
+        bt = torch.from_numpy(case.block_tokens).to(dev)
+        dl = torch.from_numpy(case.draft_lens).to(dev)
+        ctx = torch.from_numpy(case.context_lens).to(dev)
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        ws = torch.zeros(max(sda.splash_verify_accept_workspace_bytes(B, 16, V), 16), dtype=torch.uint8, device=dev)
+
+        def call(r):
+            # each call rolls context_lens back in place; nothing else reads it
+            # here, so it is left to drift rather than reset by an extra launch
+            sda.splash_verify_accept(logits[r], bt, dl, ctx, acc, nxt, workspace=ws)
+
+        for r in range(min(R, 8)):
+            call(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(max(steps, 1) * 60e-6 * 2.0e9))
+        e0.record()
+        for i in range(steps):
+            call(i % R)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        nbytes = int(case.draft_lens.sum()) * row_bytes + int(case.draft_lens.sum()) * 4 + B * 16
+        res[name] = {"B": B, "vocab": V, "rows": int(case.draft_lens.sum()), "logit_bytes": nbytes,
+                     "us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del logits, base
+    return res
 
 
 def read_ceiling_gbs(dev) -> float:

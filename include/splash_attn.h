@@ -214,6 +214,46 @@ int splash_verify_attn_splitk_merge(const uint16_t* part_o, const float* part_ls
                                     int B, int T_max, int Hq, int Hkv, int D, int num_splits,
                                     void* stream);
 
+/*
+ * splash_verify_accept -- accept the verified part of a drafted block and roll
+ * the cache back past the rest: the step after the verify pass.  The draft
+ * model proposes a block, the target checks the whole block in one forward
+ * pass, the final output is identical to autoregressive decoding, and
+ * drafting, verification, acceptance and the state update run as one unit
+ * (discuss.pytorch.kr summary, section "DFlash 2 speculative decoding as the
+ * default path").  With greedy decoding that is, for request b and
+ * d = draft_lens[b]:
+ *   block_tokens[b][0]       the last committed token, block_tokens[b][1..d-1]
+ *                            the drafts (the d tokens the verify pass attended);
+ *   logits[b][t][:]          the target's logits for the token after block
+ *                            position t (bf16, [B][T_max][V]);
+ *   y_t = argmax_v logits[b][t][v]   the largest value, compared as the exact
+ *                            value of the bf16 number (so -0 == +0); among equal
+ *                            values the lowest id;
+ *   accepted[b]   = 1 + the number of leading i < d - 1 with
+ *                   block_tokens[b][i + 1] == y_i      (block tokens whose KV
+ *                   entries stay in the cache, 1..d);
+ *   next_token[b] = y_{accepted[b] - 1}               (the target's own token);
+ *   context_lens[b] -= d - accepted[b]                 (in place).
+ * The tokens the step emits, block_tokens[b][1 .. accepted[b] - 1] and then
+ * next_token[b], are exactly those greedy autoregressive decoding emits.
+ * d = 0 is a no-op: accepted[b] = 0, next_token[b] = -1, context_lens[b]
+ * unchanged.  Rows t >= d of logits are not read.  Deterministic.
+ * Arguments: logits 16-byte aligned, V a multiple of 8 in [8, 2^30];
+ * 1 <= T_max <= 64 (SPLASH_ERR_UNSUPPORTED above); accepted and next_token are
+ * int32 [B] outputs; context_lens is read and written.  Preconditions (trusted,
+ * device memory): 0 <= draft_lens[b] <= T_max, draft_lens[b] <= context_lens[b],
+ * no logit of a read row is NaN.
+ * workspace: device memory of splash_verify_accept_workspace_bytes(B, T_max, V)
+ * bytes, 16-byte aligned, caller-owned: the partial maxima of each row's
+ * chunks (no need to clear it; calls that overlap in time must not share it).
+ * Two kernel launches.
+ */
+size_t splash_verify_accept_workspace_bytes(int B, int T_max, int V);
+int splash_verify_accept(const uint16_t* logits, const int32_t* block_tokens, const int32_t* draft_lens,
+                         int32_t* context_lens, int32_t* accepted, int32_t* next_token,
+                         int B, int T_max, int V, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for a status code (static storage, never NULL). */
 const char* splash_status_string(int status);
 

@@ -35,6 +35,8 @@ EXPORTED = (
     "splash_verify_attn_partition",
     "splash_verify_attn_split_pages",
     "splash_verify_attn_splitk_merge",
+    "splash_verify_accept_workspace_bytes",
+    "splash_verify_accept",
     "splash_status_string",
 )
 
@@ -71,10 +73,14 @@ def load_library(path: Path | None = None):
                                                  _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
     lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
     lib.splash_verify_attn_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    lib.splash_verify_accept_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.splash_verify_accept_workspace_bytes.restype = _Z
+    lib.splash_verify_accept.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]
     lib.splash_status_string.argtypes = [_I]
     lib.splash_status_string.restype = ctypes.c_char_p
     for name in EXPORTED:
-        if name not in ("splash_verify_attn_workspace_bytes", "splash_status_string"):
+        if name not in ("splash_verify_attn_workspace_bytes", "splash_verify_accept_workspace_bytes",
+                        "splash_status_string"):
             getattr(lib, name).restype = _I
     if path is None:
         _lib_handle = lib
@@ -286,3 +292,32 @@ def splash_verify_attn_splitk_merge(part_o, part_lse, out, draft_lens, stream=No
                                                 Hq, Hkv, D, S, _stream(stream))
     _check(rc, "splash_verify_attn_splitk_merge")
     return out
+
+
+def splash_verify_accept_workspace_bytes(B, T_max, V):
+    return int(_lib().splash_verify_accept_workspace_bytes(int(B), int(T_max), int(V)))
+
+
+def splash_verify_accept(logits, block_tokens, draft_lens, context_lens, accepted, next_token,
+                         workspace=None, stream=None):
+    """Greedy acceptance of a verified block; context_lens is updated in place.
+    logits bf16 [B][T_max][V]; block_tokens int32 [B][T_max]; draft_lens,
+    context_lens, accepted, next_token int32 [B].  Returns (accepted, next_token)."""
+    torch = _torch()
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B][T_max][V]")
+    B, T_max, V = (int(x) for x in logits.shape)
+    _dev(logits, "logits", (torch.bfloat16, torch.int16))
+    _dev(block_tokens, "block_tokens", (torch.int32,), (B, T_max))
+    for name, t in (("draft_lens", draft_lens), ("context_lens", context_lens), ("accepted", accepted),
+                    ("next_token", next_token)):
+        _dev(t, name, (torch.int32,), (B,))
+    need = splash_verify_accept_workspace_bytes(B, T_max, V)
+    if workspace is None:                                     # counters must start at zero
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=logits.device)
+    _dev(workspace, "workspace", (torch.uint8,))
+    rc = _lib().splash_verify_accept(logits.data_ptr(), block_tokens.data_ptr(), draft_lens.data_ptr(),
+                                     context_lens.data_ptr(), accepted.data_ptr(), next_token.data_ptr(),
+                                     B, T_max, V, workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc, "splash_verify_accept")
+    return accepted, next_token

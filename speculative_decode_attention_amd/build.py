@@ -9,7 +9,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libsplash_attn.so"
-SOURCES = ["abi.hip", "kv_append.hip", "verify_attn.hip"]
+SOURCES = ["abi.hip", "kv_append.hip", "verify_attn.hip", "accept.hip"]
 # measurement probe used by bench.py only (not part of the attention library)
 PROBE_LIB = PKG / "libsplash_probe.so"
 PROBE_SOURCES = ["read_ceiling.hip"]

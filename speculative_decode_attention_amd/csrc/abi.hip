@@ -17,6 +17,8 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int kMaxVerifyT = 16;
+constexpr int kMaxAcceptT = 64;     // the finalize kernel keeps a block on one wave
+constexpr int kMaxAcceptV = 1 << 30;
 // smallest number of pages a split is given by the preset: below this the
 // fixed cost of a workgroup (loading Q, writing partials) dominates its work
 constexpr int kMinPagesPerSplit = 8;
@@ -202,6 +204,28 @@ int splash_verify_attn_splitk_merge(const uint16_t* part_o, const float* part_ls
     TiledMergeArgs m{part_o, part_lse, out, draft_lens, B, T_max, Hq, Hkv, D, num_splits};
     return launch_splitk_merge_tiled(m, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
                                                                                       : SPLASH_ERR_LAUNCH;
+}
+
+size_t splash_verify_accept_workspace_bytes(int B, int T_max, int V) {
+    if (B < 0 || T_max < 0 || V < 8 || V > kMaxAcceptV) return 0;
+    return (size_t)B * (size_t)T_max * (size_t)accept_num_chunks(V) * sizeof(int2);
+}
+
+int splash_verify_accept(const uint16_t* logits, const int32_t* block_tokens, const int32_t* draft_lens,
+                         int32_t* context_lens, int32_t* accepted, int32_t* next_token, int B, int T_max,
+                         int V, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!logits || !block_tokens || !draft_lens || !context_lens || !accepted || !next_token)
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B < 0 || B > 65535 || T_max < 0 || V < 8 || V > kMaxAcceptV || V % 8 != 0 || !aligned16(logits))
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (T_max > kMaxAcceptT) return SPLASH_ERR_UNSUPPORTED;
+    if (B == 0) return SPLASH_OK;
+    if (T_max == 0) return SPLASH_ERR_INVALID_ARGUMENT;      // draft_lens[b] <= T_max leaves no block to accept
+    if (!workspace || !aligned16(workspace)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < splash_verify_accept_workspace_bytes(B, T_max, V)) return SPLASH_ERR_WORKSPACE_TOO_SMALL;
+    AcceptArgs a{logits, block_tokens, draft_lens, context_lens, accepted, next_token,
+                 static_cast<int2*>(workspace), B, T_max, V, accept_num_chunks(V)};
+    return launch_verify_accept(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -52,6 +52,18 @@ struct TiledMergeArgs {
 };
 
 
+struct AcceptArgs {
+    const uint16_t* logits;    // bf16 [B][T_max][V]
+    const int32_t* block_tokens;
+    const int32_t* draft_lens;
+    int32_t* context_lens;
+    int32_t* accepted;
+    int32_t* next_token;
+    int2* part;                // [B][T_max][num_chunks] (value bits, id) partials
+    int B, T_max, V, num_chunks;
+};
+
+constexpr int kAcceptChunk = 8192;   // logits per workgroup of the argmax kernel
 
 constexpr int kPage = 16;            // tokens per page (the compiled page size)
 constexpr int kPagesPerIter = 4;    // pages a workgroup of the partition kernel takes per step
@@ -61,5 +73,7 @@ bool verify_supported(int D, int G);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_splitk_merge_tiled(const TiledMergeArgs& a, hipStream_t stream);
+int accept_num_chunks(int V);
+hipError_t launch_verify_accept(const AcceptArgs& a, hipStream_t stream);
 
 }  // namespace splash

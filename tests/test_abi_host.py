@@ -153,6 +153,33 @@ def test_partition_rejects_bad_arguments(lib):
     assert p(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
 
 
+def test_accept_workspace_arithmetic(lib):
+    ws = lib.splash_verify_accept_workspace_bytes
+    # 19 chunks of 8192 logits per row, a (value, id) pair each
+    assert ws(16, 16, 151936) == 16 * 16 * 19 * 8
+    assert ws(1, 16, 8192) == 16 * 8 and ws(1, 16, 8200) == 16 * 2 * 8
+    assert ws(100, 1, 8) == 100 * 8
+    assert ws(0, 16, 64) == 0 and ws(2, 3, 4) == 0             # V below 8: no valid size
+
+
+def test_accept_rejects_bad_arguments(lib):
+    a = lib.splash_verify_accept
+    ok = [FAKE] * 6 + [4, 16, 151936, FAKE, 1 << 20, None]
+    assert a(*ok[:5], None, *ok[6:]) == sda.SPLASH_ERR_INVALID_ARGUMENT       # next_token missing
+    args = list(ok); args[8] = 151937                                          # V not a multiple of 8
+    assert a(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    args = list(ok); args[0] = FAKE + 2                                        # misaligned logits
+    assert a(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    args = list(ok); args[7] = 65                                              # one wave holds a block
+    assert a(*args) == sda.SPLASH_ERR_UNSUPPORTED
+    args = list(ok); args[10] = 4 * 16 * 19 * 8 - 1                           # workspace one byte short
+    assert a(*args) == sda.SPLASH_ERR_WORKSPACE_TOO_SMALL
+    args = list(ok); args[9] = None
+    assert a(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    args = list(ok); args[6] = 0                                               # empty batch: nothing launched
+    assert a(*args) == sda.SPLASH_OK
+
+
 def test_binding_fails_loudly_without_the_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         sda.load_library(tmp_path / "missing.so")
