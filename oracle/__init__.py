@@ -54,6 +54,8 @@ def _declare(lib):
                                                  _P, _P]
     lib.splash_ref_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I]
     lib.splash_ref_verify_accept.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I]
+    lib.splash_ref_verify_attn_masked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                                  _I, _I, _I, _I, _I, _I, _I, _D, _P]
     lib.splash_ref_num_threads.argtypes = []
     lib.splash_ref_num_threads.restype = ctypes.c_int
     lib.ref_quantize_row.argtypes = [_P, _I, _P, _P]
@@ -63,7 +65,8 @@ def _declare(lib):
     lib.ref_f16_to_f32.argtypes = [ctypes.c_uint16]
     lib.ref_f16_to_f32.restype = ctypes.c_float
     for f in ("splash_ref_kv_append_int8", "splash_ref_verify_attn", "splash_ref_verify_attn_rows",
-              "splash_ref_verify_attn_split", "splash_ref_splitk_merge", "splash_ref_verify_accept"):
+              "splash_ref_verify_attn_split", "splash_ref_splitk_merge", "splash_ref_verify_accept",
+              "splash_ref_verify_attn_masked"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -148,6 +151,24 @@ class Oracle:
             float(sm_scale))
         if rc:
             raise ValueError(f"oracle verify_attn rejected its arguments (rc={rc})")
+        return out
+
+    def verify_attn_masked(self, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                           draft_lens, Hkv, sm_scale, block_masks, out=None):
+        """As verify_attn with block_masks uint32 [B][T_max] (bit u of row t: draft t sees draft u)."""
+        B, T_max, Hq, D = q.shape
+        num_pages, _, P, _ = k_pool.shape
+        masks = np.ascontiguousarray(block_masks, dtype=np.uint32)
+        assert masks.shape == (B, T_max)
+        if out is None:
+            out = np.full(q.shape, np.nan, dtype=np.float64)
+        rc = self.lib.splash_ref_verify_attn_masked(
+            self._ptr(q), self._ptr(out), self._ptr(k_pool), self._ptr(v_pool),
+            self._ptr(k_scale), self._ptr(v_scale), self._ptr(block_table), block_table.shape[1],
+            self._ptr(context_lens), self._ptr(draft_lens), B, T_max, Hq, Hkv, D, P, num_pages,
+            float(sm_scale), self._ptr(masks))
+        if rc:
+            raise ValueError(f"oracle verify_attn_masked rejected its arguments (rc={rc})")
         return out
 
     def verify_attn_rows(self, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,

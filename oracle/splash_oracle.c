@@ -213,25 +213,42 @@ int splash_ref_kv_append_int8(const void* k_new, const void* v_new, int src_dtyp
 
 /*
  * One output row: draft t of request b, query head h, attending over the
- * keys j in [j_lo, min(j_hi, pos_t + 1)), where pos_t = n - d + t.
+ * keys j in [j_lo, j_hi) that it sees.  Causally (mask == NULL) that is
+ * j <= pos_t, pos_t = n - d + t.  With a block mask (the tree of candidates
+ * that verification checks at once, DFlash 2 section of the summary: several
+ * candidate tokens per position), draft t sees every key before the block and
+ * the block key of draft u exactly when bit u of *mask is set.
  * Writes the normalised row to out_row (D doubles) and returns the natural
- * log-sum-exp of the scaled scores; an empty range gives -inf and a zero row.
+ * log-sum-exp of the scaled scores; no visible key gives -inf and a zero row.
  */
+static int key_visible(int j, int blk0, int n, int pos, const uint32_t* mask)
+{
+    if (!mask) return j <= pos;
+    if (j < blk0) return 1;
+    if (j >= n) return 0;
+    return (int)((*mask >> (j - blk0)) & 1u);
+}
+
 static double attend_row(const uint16_t* q_row,
                          const int8_t* k_pool, const int8_t* v_pool,
                          const uint16_t* k_scale, const uint16_t* v_scale,
                          const int32_t* bt_row, int b_ctx, int b_draft, int t, int g,
                          int Hkv, int D, int P, double sm_scale,
-                         int j_lo, int j_hi, double* z, double* out_row)
+                         int j_lo, int j_hi, const uint32_t* mask, double* z, double* out_row)
 {
-    int pos = b_ctx - b_draft + t;              /* this draft's own position */
-    int end = pos + 1 < j_hi ? pos + 1 : j_hi;  /* causal: keys 0..pos        */
+    int blk0 = b_ctx - b_draft;                 /* first key of the block     */
+    int pos = blk0 + t;                         /* this draft's own position */
+    int end = mask ? (b_ctx < j_hi ? b_ctx : j_hi)
+                   : (pos + 1 < j_hi ? pos + 1 : j_hi);   /* causal: keys 0..pos */
     for (int d = 0; d < D; ++d) out_row[d] = 0.0;
-    if (end <= j_lo) return -INFINITY;
+    int seen = 0;
+    for (int j = j_lo; j < end; ++j) seen += key_visible(j, blk0, b_ctx, pos, mask);
+    if (!seen) return -INFINITY;
 
     /* scores z_j = sm_scale * <q, K_hat_j>, K_hat_j = scale_j * codes_j */
     double zmax = -INFINITY;
     for (int j = j_lo; j < end; ++j) {
+        if (!key_visible(j, blk0, b_ctx, pos, mask)) continue;
         int page = bt_row[j / P], slot = j % P;
         double ks = (double)ref_f16_to_f32(k_scale[s_index(page, g, slot, Hkv, P)]);
         double dot = 0.0;
@@ -245,6 +262,7 @@ static double attend_row(const uint16_t* q_row,
     /* softmax weights relative to the max, then the weighted sum of V_hat */
     double wsum = 0.0;
     for (int j = j_lo; j < end; ++j) {
+        if (!key_visible(j, blk0, b_ctx, pos, mask)) continue;
         int page = bt_row[j / P], slot = j % P;
         double w = exp(z[j - j_lo] - zmax);
         double vs = (double)ref_f16_to_f32(v_scale[s_index(page, g, slot, Hkv, P)]);
@@ -277,14 +295,17 @@ static int check_attn_args(const void* q, const void* out, const void* k_pool, c
 /*
  * splash_ref_verify_attn: fp64 block-verify attention.  out is fp64
  * [B][T_max][Hq][D]; rows t >= draft_lens[b] are left untouched.
+ * splash_ref_verify_attn_masked: the same with block_masks uint32 [B][T_max]
+ * (bit u of block_masks[b][t]: draft t sees draft u) in place of the causal
+ * chain inside the block.
  */
-int splash_ref_verify_attn(const uint16_t* q, double* out,
-                           const int8_t* k_pool, const int8_t* v_pool,
-                           const uint16_t* k_scale, const uint16_t* v_scale,
-                           const int32_t* block_table, int max_pages_per_seq,
-                           const int32_t* context_lens, const int32_t* draft_lens,
-                           int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
-                           double sm_scale)
+static int verify_attn_impl(const uint16_t* q, double* out,
+                            const int8_t* k_pool, const int8_t* v_pool,
+                            const uint16_t* k_scale, const uint16_t* v_scale,
+                            const int32_t* block_table, int max_pages_per_seq,
+                            const int32_t* context_lens, const int32_t* draft_lens,
+                            int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                            double sm_scale, const uint32_t* block_masks)
 {
     int rc = check_attn_args(q, out, k_pool, v_pool, k_scale, v_scale, block_table,
                              context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages,
@@ -310,11 +331,38 @@ int splash_ref_verify_attn(const uint16_t* q, double* out,
         attend_row(q + row, k_pool, v_pool, k_scale, v_scale,
                    block_table + (size_t)b * max_pages_per_seq,
                    context_lens[b], draft_lens[b], t, h / group, Hkv, D, P, sm_scale,
-                   0, context_lens[b], z, out + row);
+                   0, context_lens[b], block_masks ? block_masks + (size_t)b * T_max + t : NULL,
+                   z, out + row);
     }
     free(z);
     }
     return fail ? REF_ERR_ARG : REF_OK;
+}
+
+int splash_ref_verify_attn(const uint16_t* q, double* out,
+                           const int8_t* k_pool, const int8_t* v_pool,
+                           const uint16_t* k_scale, const uint16_t* v_scale,
+                           const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* context_lens, const int32_t* draft_lens,
+                           int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                           double sm_scale)
+{
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale, NULL);
+}
+
+int splash_ref_verify_attn_masked(const uint16_t* q, double* out,
+                                  const int8_t* k_pool, const int8_t* v_pool,
+                                  const uint16_t* k_scale, const uint16_t* v_scale,
+                                  const int32_t* block_table, int max_pages_per_seq,
+                                  const int32_t* context_lens, const int32_t* draft_lens,
+                                  int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                                  double sm_scale, const uint32_t* block_masks)
+{
+    if (!block_masks || T_max > 32) return REF_ERR_ARG;
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale,
+                            block_masks);
 }
 
 /*
@@ -356,7 +404,7 @@ int splash_ref_verify_attn_rows(const uint16_t* q,
         attend_row(q + row, k_pool, v_pool, k_scale, v_scale,
                    block_table + (size_t)b * max_pages_per_seq,
                    context_lens[b], draft_lens[b], t, h / group, Hkv, D, P, sm_scale,
-                   0, context_lens[b], z, out_rows + (size_t)i * D);
+                   0, context_lens[b], NULL, z, out_rows + (size_t)i * D);
     }
     free(z);
     }
@@ -410,7 +458,7 @@ int splash_ref_verify_attn_split(const uint16_t* q,
         part_lse[prow] = attend_row(q + qrow, k_pool, v_pool, k_scale, v_scale,
                                     block_table + (size_t)b * max_pages_per_seq,
                                     context_lens[b], draft_lens[b], t, h / group, Hkv, D, P,
-                                    sm_scale, (int)lo, (int)hi, z, part_o + prow * D);
+                                    sm_scale, (int)lo, (int)hi, NULL, z, part_o + prow * D);
     }
     free(z);
     }

@@ -369,3 +369,31 @@ def make_accept_case(seed: int, *, B: int, T_max: int, V: int = VOCAB, draft_len
     ctx = np.full(B, context_base, dtype=np.int32) + dl
     return AcceptCase(logits=_bf16_bits(x), block_tokens=bt, draft_lens=dl, context_lens=ctx,
                       planted_tokens=planted, planted_accept=acc)
+
+
+def tree_block_masks(seed: int, draft_lens, T_max: int) -> np.ndarray:
+    """Random candidate trees over each request's block: draft t > 0 hangs under a
+    drawn earlier draft; bit u of mask[b][t] is set for t itself and each
+    ancestor u (the drafts a tree-verify pass lets draft t see).  uint32 [B][T_max]."""
+    rng = np.random.default_rng(seed)
+    dl = np.asarray(draft_lens, dtype=np.int64)
+    masks = np.zeros((len(dl), T_max), dtype=np.uint32)
+    for b, d in enumerate(dl):
+        parent = [-1] + [int(rng.integers(0, t)) for t in range(1, int(d))]
+        for t in range(int(d)):
+            m, u = 0, t
+            while u >= 0:
+                m |= 1 << u
+                u = parent[u]
+            masks[b, t] = m
+    return masks
+
+
+def chain_block_masks(draft_lens, T_max: int) -> np.ndarray:
+    """The causal chain as block masks: draft t sees drafts 0..t."""
+    dl = np.asarray(draft_lens, dtype=np.int64)
+    masks = np.zeros((len(dl), T_max), dtype=np.uint32)
+    for b, d in enumerate(dl):
+        for t in range(int(d)):
+            masks[b, t] = (1 << (t + 1)) - 1
+    return masks

@@ -20,6 +20,8 @@ pins come from the mathematics and from library routines):
   split + merge          the split path merged by the log-sum-exp identity ==
                          unsplit; merge closed forms (equal weights, one live
                          split, shift invariance)
+  tree masks             the dense brute force with the same mask; the chain
+                         mask bit-identical to the causal block
   acceptance             spiked logits with known greedy tokens (planted
                          acceptance points, no block, whole block kept); ties
                          to the lowest id, signed zeros, negatives; brute-force
@@ -517,6 +519,36 @@ def pin_merge_closed_forms(orc, seed=30):
 
 
 # --------------------------------------------------------------------------
+# tree-shaped block masks
+# --------------------------------------------------------------------------
+def pin_tree_mask_dense(orc, seed=31):
+    """Random candidate trees: the masked oracle against the dense brute force
+    given the same mask (whole-matrix numpy, no paging)."""
+    for i, kw in enumerate([{}, dict(context_lens=[20, 16], draft_lens=[5, 16], T_max=16)]):
+        wl = _small_direct(seed + i, **kw)
+        masks = synth.tree_block_masks(seed + 10 + i, wl.draft_lens, wl.T_max)
+        out = orc.verify_attn_masked(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                                     wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale, masks)
+        for b in range(wl.B):
+            k_hat, v_hat = dense_from_direct(wl, b)
+            d = int(wl.draft_lens[b])
+            ref = dense_block_attention(bf16_value(wl.q[b, :d]), k_hat, v_hat, wl.sm_scale, masks[b, :d])
+            assert rel_err(out[b, :d], ref) <= 1e-12, rel_err(out[b, :d], ref)
+            assert np.all(np.isnan(out[b, d:]))
+
+
+def pin_tree_mask_chain_is_causal(orc, seed=32):
+    """The chain mask (draft t sees drafts 0..t) is the causal block: bit-identical rows."""
+    wl = _small_direct(seed, context_lens=[30, 16, 40], draft_lens=[5, 16, 1], T_max=16, B=3)
+    causal = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                             wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    chain = orc.verify_attn_masked(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                                   wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale,
+                                   synth.chain_block_masks(wl.draft_lens, wl.T_max))
+    assert np.array_equal(causal, chain, equal_nan=True)
+
+
+# --------------------------------------------------------------------------
 # acceptance of a verified block
 # --------------------------------------------------------------------------
 def _check_planted(orc, case):
@@ -617,6 +649,8 @@ ALL_PINS = [
     pin_rows_api_matches_full,
     pin_split_equals_unsplit,
     pin_merge_closed_forms,
+    pin_tree_mask_dense,
+    pin_tree_mask_chain_is_causal,
     pin_accept_planted,
     pin_accept_ties_lowest_id,
     pin_accept_equals_greedy_decoding,

@@ -54,6 +54,10 @@ MUTANTS = {
     "split_range_shift": ("long lo = (long)s * L * P, hi", "long lo = (long)s * L * P + 1, hi"),
     "merge_weight_sign": ("double w = exp(l - M);", "double w = exp(M - l);"),
     "merge_no_normalise": ("for (int d = 0; d < D; ++d) o[d] /= wsum;", ""),
+    # tree masks
+    "tree_mask_ignored": ("    if (!mask) return j <= pos;", "    if (mask) return j <= pos;"),
+    "tree_mask_bit_shift": ("return (int)((*mask >> (j - blk0)) & 1u);", "return (int)((*mask >> (j - blk0 + 1)) & 1u);"),
+    "tree_mask_hides_context": ("    if (j < blk0) return 1;", "    if (j < blk0) return j + 1 < blk0;"),
     # acceptance
     "accept_ties_highest": ("if (x > bv) { bv = x; best = v; }", "if (x >= bv) { bv = x; best = v; }"),
     "accept_compares_bits": ("float x = bf16_to_f32(row[v]);", "float x = (float)row[v];"),
