@@ -221,9 +221,9 @@ int splash_ref_kv_append_int8(const void* k_new, const void* v_new, int src_dtyp
  * Writes the normalised row to out_row (D doubles) and returns the natural
  * log-sum-exp of the scaled scores; no visible key gives -inf and a zero row.
  */
-static int key_visible(int j, int blk0, int n, int pos, const uint32_t* mask)
+static int key_visible(int j, int blk0, int n, const uint32_t* mask)
 {
-    if (!mask) return j <= pos;
+    if (!mask) return 1;                        /* causal: the range end bounds the keys */
     if (j < blk0) return 1;
     if (j >= n) return 0;
     return (int)((*mask >> (j - blk0)) & 1u);
@@ -242,13 +242,13 @@ static double attend_row(const uint16_t* q_row,
                    : (pos + 1 < j_hi ? pos + 1 : j_hi);   /* causal: keys 0..pos */
     for (int d = 0; d < D; ++d) out_row[d] = 0.0;
     int seen = 0;
-    for (int j = j_lo; j < end; ++j) seen += key_visible(j, blk0, b_ctx, pos, mask);
+    for (int j = j_lo; j < end; ++j) seen += key_visible(j, blk0, b_ctx, mask);
     if (!seen) return -INFINITY;
 
     /* scores z_j = sm_scale * <q, K_hat_j>, K_hat_j = scale_j * codes_j */
     double zmax = -INFINITY;
     for (int j = j_lo; j < end; ++j) {
-        if (!key_visible(j, blk0, b_ctx, pos, mask)) continue;
+        if (!key_visible(j, blk0, b_ctx, mask)) continue;
         int page = bt_row[j / P], slot = j % P;
         double ks = (double)ref_f16_to_f32(k_scale[s_index(page, g, slot, Hkv, P)]);
         double dot = 0.0;
@@ -262,7 +262,7 @@ static double attend_row(const uint16_t* q_row,
     /* softmax weights relative to the max, then the weighted sum of V_hat */
     double wsum = 0.0;
     for (int j = j_lo; j < end; ++j) {
-        if (!key_visible(j, blk0, b_ctx, pos, mask)) continue;
+        if (!key_visible(j, blk0, b_ctx, mask)) continue;
         int page = bt_row[j / P], slot = j % P;
         double w = exp(z[j - j_lo] - zmax);
         double vs = (double)ref_f16_to_f32(v_scale[s_index(page, g, slot, Hkv, P)]);

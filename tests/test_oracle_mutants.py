@@ -36,10 +36,8 @@ MUTANTS = {
     "append_v_scale_into_k": ("k_scale[s_index(page, g, slot, Hkv, P)] = s16;",
                               "v_scale[s_index(page, g, slot, Hkv, P)] = s16;"),
     # attention
-    "causal_excludes_self": ("int end = pos + 1 < j_hi ? pos + 1 : j_hi;",
-                             "int end = pos < j_hi ? pos : j_hi;"),
-    "causal_sees_next": ("int end = pos + 1 < j_hi ? pos + 1 : j_hi;",
-                         "int end = pos + 2 < j_hi ? pos + 2 : j_hi;"),
+    "causal_excludes_self": (": (pos + 1 < j_hi ? pos + 1 : j_hi);", ": (pos < j_hi ? pos : j_hi);"),
+    "causal_sees_next": (": (pos + 1 < j_hi ? pos + 1 : j_hi);", ": (pos + 2 < j_hi ? pos + 2 : j_hi);"),
     "no_sm_scale": ("z[j - j_lo] = sm_scale * dot;", "z[j - j_lo] = dot;"),
     "k_uses_v_scale": ("double ks = (double)ref_f16_to_f32(k_scale[",
                        "double ks = (double)ref_f16_to_f32(v_scale["),
@@ -55,7 +53,7 @@ MUTANTS = {
     "merge_weight_sign": ("double w = exp(l - M);", "double w = exp(M - l);"),
     "merge_no_normalise": ("for (int d = 0; d < D; ++d) o[d] /= wsum;", ""),
     # tree masks
-    "tree_mask_ignored": ("    if (!mask) return j <= pos;", "    if (mask) return j <= pos;"),
+    "tree_mask_ignored": ("    if (!mask) return 1;", "    return 1;"),
     "tree_mask_bit_shift": ("return (int)((*mask >> (j - blk0)) & 1u);", "return (int)((*mask >> (j - blk0 + 1)) & 1u);"),
     "tree_mask_hides_context": ("    if (j < blk0) return 1;", "    if (j < blk0) return j + 1 < blk0;"),
     # acceptance
