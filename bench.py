@@ -187,6 +187,13 @@ def main():
         sda.splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t, ctx,
                                wl.sm_scale, num_splits=S_req, workspace=ws)
 
+    # the same call with a tree-shaped block mask (random candidate tree)
+    tree = torch.from_numpy(synth.tree_block_masks(77, wl.draft_lens, T).view(np.int32)).to(dev)
+
+    def verify_tree(r):
+        sda.splash_verify_attn_masked(q, out, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t, tree, ctx,
+                                      wl.sm_scale, num_splits=S_req, workspace=ws)
+
     def partition(r):
         sda.splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t,
                                          ctx, wl.sm_scale, S, part_o, part_lse)
@@ -199,7 +206,8 @@ def main():
     # one graph of C consecutive calls on replicas 0..C-1
     C = max(d for d in range(1, R + 1) if args.steps % d == 0)
     graphs = {}
-    for name, fn in (("step", step), ("verify", verify)):
+    verify_tree(0)
+    for name, fn in (("step", step), ("verify", verify), ("verify_tree", verify_tree)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             for r in range(C):
@@ -229,6 +237,7 @@ def main():
     step_bytes = verify_bytes(ctx, Hkv, D, T, Hq) + append_bytes(T, Hkv, D)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     us_verify = timed_replays(graphs["verify"], args.steps, args.warmup) * 1e3
+    us_tree = timed_replays(graphs["verify_tree"], args.steps, args.warmup) * 1e3
 
     # the partition kernel alone, launched back to back on its stream: one event
     # pair brackets the launches (queued behind a sleep, so the host's launch
@@ -299,6 +308,7 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8",
                    "splits": S, "replicas": R, "calls_per_graph": C, "step_bytes": step_bytes,
                    "verify_us_per_call": round(us_verify, 2),
+                   "verify_tree_mask_us_per_call": round(us_tree, 2),
                    "partition_us_mall_warm": round(part_us_warm, 3),
                    "hbm_read_ceiling_pages_gbs": round(stream_gbs, 1),
                    "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)},

@@ -168,6 +168,29 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * splash_verify_attn_masked -- splash_verify_attn with a tree-shaped mask
+ * inside the block instead of the causal chain.  DFlash 2's path selector picks
+ * a coherent path among several candidate tokens per position (discuss.pytorch.kr
+ * summary, DFlash 2 section); checking several candidates in one pass makes the
+ * block a tree.  Draft t of request b attends to every key before the block
+ * (positions < context_lens[b] - draft_lens[b]) and to the block key of draft u
+ * exactly when bit u of block_masks[b][t] is set (uint32 [B][T_max], device;
+ * bits u >= draft_lens[b] are ignored).  The chain masks (bits 0..t) give
+ * splash_verify_attn's result bit for bit.  Precondition: bit t of
+ * block_masks[b][t] is set (a draft sees itself).  Everything else as
+ * splash_verify_attn; block_masks == NULL is SPLASH_ERR_INVALID_ARGUMENT.
+ */
+int splash_verify_attn_masked(const uint16_t* q, uint16_t* out,
+                              const int8_t* k_pool, const int8_t* v_pool,
+                              const uint16_t* k_scale, const uint16_t* v_scale,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* context_lens, const int32_t* draft_lens,
+                              const uint32_t* block_masks,
+                              int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                              int max_context_len, float sm_scale, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * splash_verify_attn_partition -- the first half of splash_verify_attn on its
  * own: for each context split s (pages [s*L, (s+1)*L) with
  * L = splash_verify_attn_split_pages(...)), write for draft t < draft_lens[b]

@@ -32,6 +32,7 @@ EXPORTED = (
     "splash_verify_attn_default_splits",
     "splash_verify_attn_workspace_bytes",
     "splash_verify_attn",
+    "splash_verify_attn_masked",
     "splash_verify_attn_partition",
     "splash_verify_attn_split_pages",
     "splash_verify_attn_splitk_merge",
@@ -69,6 +70,8 @@ def load_library(path: Path | None = None):
     lib.splash_verify_attn_workspace_bytes.restype = _Z
     lib.splash_verify_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_verify_attn_masked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,
+                                              _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
     lib.splash_verify_attn_partition.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                  _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
     lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
@@ -215,6 +218,21 @@ def splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, co
     workspace: a byte tensor of at least splash_verify_attn_workspace_bytes(...)
     for the splits that run, or None to let this binding allocate one with torch.
     """
+    return _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
+                   max_context_len, sm_scale, num_splits, workspace, stream, None)
+
+
+def splash_verify_attn_masked(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                              draft_lens, block_masks, max_context_len, sm_scale, num_splits=0,
+                              workspace=None, stream=None):
+    """splash_verify_attn with a tree-shaped block mask: block_masks int32/uint32
+    [B][T_max], bit u of row t lets draft t see draft u."""
+    return _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
+                   max_context_len, sm_scale, num_splits, workspace, stream, block_masks)
+
+
+def _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
+            max_context_len, sm_scale, num_splits, workspace, stream, block_masks):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B][T_max][Hq][D]")
@@ -235,12 +253,21 @@ def splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, co
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         _dev(workspace, "workspace", (torch.uint8, torch.int8, torch.float32))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    rc = _lib().splash_verify_attn(
-        q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
-        v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),
-        draft_lens.data_ptr(), B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len),
-        float(sm_scale), int(S_req), ws_ptr, ws_bytes, _stream(stream))
-    _check(rc, "splash_verify_attn")
+    if block_masks is None:
+        rc = _lib().splash_verify_attn(
+            q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),
+            draft_lens.data_ptr(), B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len),
+            float(sm_scale), int(S_req), ws_ptr, ws_bytes, _stream(stream))
+        _check(rc, "splash_verify_attn")
+    else:
+        _dev(block_masks, "block_masks", (torch.int32,), (B, T_max))
+        rc = _lib().splash_verify_attn_masked(
+            q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),
+            draft_lens.data_ptr(), block_masks.data_ptr(), B, T_max, Hq, Hkv, D, P, num_pages,
+            int(max_context_len), float(sm_scale), int(S_req), ws_ptr, ws_bytes, _stream(stream))
+        _check(rc, "splash_verify_attn_masked")
     return out
 
 

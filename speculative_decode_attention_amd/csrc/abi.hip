@@ -133,12 +133,12 @@ size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int n
     return align_up(rows * D * 2, 256) + align_up(rows * sizeof(float), 256);
 }
 
-int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
-                       const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
-                       int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
-                       int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
-                       int max_context_len, float sm_scale, int num_splits, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                            const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                            int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
+                            int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                            int max_context_len, float sm_scale, int num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream, const uint32_t* block_masks) {
     int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                                  draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
                                  max_context_len, sm_scale);
@@ -154,6 +154,7 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
     VerifyArgs a{q, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, block_table,
                  max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale, S, L,
                  num_pages};
+    a.block_masks = block_masks;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (S == 1) {
         a.out = out;
@@ -168,6 +169,29 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
     if (launch_verify_partition(a, st) != hipSuccess) return SPLASH_ERR_LAUNCH;
     TiledMergeArgs m{a.part_h, a.part_hlse, out, draft_lens, B, T_max, Hq, Hkv, D, S};
     return launch_splitk_merge_tiled(m, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
+}
+
+int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                       const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
+                       int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                       int max_context_len, float sm_scale, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr);
+}
+
+int splash_verify_attn_masked(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                              const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                              int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
+                              const uint32_t* block_masks, int B, int T_max, int Hq, int Hkv, int D, int P,
+                              int num_pages, int max_context_len, float sm_scale, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_masks) return SPLASH_ERR_INVALID_ARGUMENT;
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, block_masks);
 }
 
 int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,

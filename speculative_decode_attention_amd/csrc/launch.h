@@ -41,6 +41,7 @@ struct VerifyArgs {
     int num_splits;            // grid size along the context (S used in the layouts)
     int pages_per_split;       // L, a multiple of kPagesPerIter
     int num_pages;             // pool size; page ids are clamped into [0, num_pages)
+    const uint32_t* block_masks = nullptr;   // [B][T_max] bit u of row t: draft t sees draft u; null: causal
 };
 
 struct TiledMergeArgs {

@@ -180,7 +180,8 @@ struct Cfg {
     static constexpr int PBUF = kPagesPerIter * NT32 * 64 * 16;     // [page][32-row tile][lane][16 B]
     static constexpr int M_OFF = P_OFF + 2 * PBUF;                  // [row][page] maxima or row sums
     static constexpr int R_OFF = M_OFF + NT * 16 * kPagesPerIter * 4;   // [row] O rescale factors / references
-    static constexpr int TOTAL = R_OFF + NT * 16 * 4;
+    static constexpr int MASK_OFF = R_OFF + NT * 16 * 4;          // [16] block masks of the request's drafts
+    static constexpr int TOTAL = MASK_OFF + 16 * 4;
     static constexpr int Q_OFF = V_OFF + SLOT;        // start-up only: Q over the V slots 1.. onwards
     static constexpr int QBYTES = NT * 16 * D * 2;
     static_assert(D % 64 == 0 && PVW >= 1, "head dim must be a multiple of 64");
@@ -209,7 +210,7 @@ __device__ __forceinline__ int k_swizzle(int slot) {
 //  * Output wave c = v - 4: copies page c of every step (K rows, scales, page
 //    id, V rows) and owns columns [32 c SPW, 32 (c + 1) SPW) of all rows for
 //    P V, so every V code is converted once.
-template <int D, int G, int NTU>
+template <int D, int G, int NTU, bool MASKED>
 __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds, const int b, const int g,
                                                const int s, const int dl, const int ctx, const int pg_begin,
                                                const int pg_end) {
@@ -320,6 +321,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         if (lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + c) * 4) = ids0;
         if (c == 0 && lane < 2 * kWaves / 4)                  // both flag buffers start clear
             *reinterpret_cast<uint32_t*>(lds + C::F_OFF + 4 * lane) = 0u;
+        if (MASKED && c == 1 && lane < 16)                    // the drafts' block masks
+            *reinterpret_cast<uint32_t*>(lds + C::MASK_OFF + 4 * lane) =
+                lane < a.T_max ? a.block_masks[(size_t)b * a.T_max + lane] : 0u;
 #pragma unroll
         for (int j = 0; j < kKAhead; ++j) issue_k(j, clamp_page(idj[j]));
         issue_v(0, clamp_page(idj[0]));
@@ -553,10 +557,25 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 #pragma unroll
                     for (int j = 0; j < 4; ++j) zs[k][i][j] = __builtin_fmaf(acc[i][j], kc[j], nmr[i]);
                     if (masked) {
-                        const int row = 16 * (t0 + i) + li;   // last key the row may see; -1: padded row
-                        const int last_key = row < rows ? ctx - dl + row / G : -1;
+                        // a row sees the keys before the block and the block key of
+                        // draft u when bit u of its mask is set (the causal chain:
+                        // bits 0..t); a padded row sees nothing here
+                        const int row = 16 * (t0 + i) + li;
+                        if constexpr (MASKED) {
+                            const int blk0 = ctx - dl;
+                            const uint32_t mrow = row < rows ? *reinterpret_cast<const uint32_t*>(lds + C::MASK_OFF + 4 * (row / G)) : 0u;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) zs[k][i][j] = kl + j <= last_key ? zs[k][i][j] : -INFINITY;
+                            for (int j = 0; j < 4; ++j) {
+                                const int key = kl + j, u = key - blk0;
+                                const bool inblk = (unsigned)u < (unsigned)dl;
+                                const bool vis = (row < rows) & ((key < blk0) | (inblk & (((mrow >> (u & 31)) & 1u) != 0u)));
+                                zs[k][i][j] = vis ? zs[k][i][j] : -INFINITY;
+                            }
+                        } else {
+                            const int last_key = row < rows ? ctx - dl + row / G : -1;   // -1: padded row
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) zs[k][i][j] = kl + j <= last_key ? zs[k][i][j] : -INFINITY;
+                        }
                     }
                     const float mx = fmaxf(fmaxf(zs[k][i][0], zs[k][i][1]), fmaxf(zs[k][i][2], zs[k][i][3]));
                     exceed |= mx > (bigk ? fminf(thr[i], 0.0f) : thr[i]);
@@ -796,19 +815,19 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 }
 
 // run the body with the number of row tiles in use as a compile-time constant
-template <int D, int G, int NTU>
+template <int D, int G, int NTU, bool MASKED>
 __device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a, uint8_t* lds, int b, int g,
                                                int s, int dl, int ctx, int pg_begin, int pg_end) {
     if constexpr (NTU > 1) {
         if (nt_used < NTU) {
-            dispatch_tiles<D, G, NTU - 1>(nt_used, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+            dispatch_tiles<D, G, NTU - 1, MASKED>(nt_used, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
             return;
         }
     }
-    partition_body<D, G, NTU>(a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+    partition_body<D, G, NTU, MASKED>(a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
 }
 
-template <int D, int G>
+template <int D, int G, bool MASKED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void verify_partition_kernel(const VerifyArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg<D, G>::TOTAL];
@@ -834,7 +853,7 @@ void verify_partition_kernel(const VerifyArgs a) {
         }
         return;
     }
-    dispatch_tiles<D, G, G>((rows + 15) >> 4, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+    dispatch_tiles<D, G, G, MASKED>((rows + 15) >> 4, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
 }
 
 // ---------------------------------------------------------------------------
@@ -963,7 +982,10 @@ static hipError_t launch_partition_dg(const VerifyArgs& a, hipStream_t stream) {
     const long blocks = (long)a.B * a.Hkv * a.num_splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((verify_partition_kernel<D, G>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+    if (a.block_masks != nullptr)
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, true>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, false>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

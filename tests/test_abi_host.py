@@ -153,6 +153,15 @@ def test_partition_rejects_bad_arguments(lib):
     assert p(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
 
 
+def test_masked_verify_needs_its_masks(lib):
+    args = [FAKE] * 7 + [2048, FAKE, FAKE, None, 1, 16, 24, 4, 256, 16, 65536, 32768,
+                         ctypes.c_float(0.0625), 0, FAKE, 1 << 30, None]
+    assert lib.splash_verify_attn_masked(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT   # no masks
+    args[10] = FAKE
+    args[0] = None
+    assert lib.splash_verify_attn_masked(*args) == sda.SPLASH_ERR_INVALID_ARGUMENT
+
+
 def test_accept_workspace_arithmetic(lib):
     ws = lib.splash_verify_accept_workspace_bytes
     # 19 chunks of 8192 logits per row, a (value, id) pair each
