@@ -56,6 +56,8 @@ def _declare(lib):
     lib.splash_ref_verify_accept.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I]
     lib.splash_ref_verify_attn_masked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                   _I, _I, _I, _I, _I, _I, _I, _D, _P]
+    lib.splash_ref_verify_attn_window.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                                  _I, _I, _I, _I, _I, _I, _I, _D, _I]
     lib.splash_ref_num_threads.argtypes = []
     lib.splash_ref_num_threads.restype = ctypes.c_int
     lib.ref_quantize_row.argtypes = [_P, _I, _P, _P]
@@ -66,7 +68,7 @@ def _declare(lib):
     lib.ref_f16_to_f32.restype = ctypes.c_float
     for f in ("splash_ref_kv_append_int8", "splash_ref_verify_attn", "splash_ref_verify_attn_rows",
               "splash_ref_verify_attn_split", "splash_ref_splitk_merge", "splash_ref_verify_accept",
-              "splash_ref_verify_attn_masked"):
+              "splash_ref_verify_attn_masked", "splash_ref_verify_attn_window"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -169,6 +171,22 @@ class Oracle:
             float(sm_scale), self._ptr(masks))
         if rc:
             raise ValueError(f"oracle verify_attn_masked rejected its arguments (rc={rc})")
+        return out
+
+    def verify_attn_window(self, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                           draft_lens, Hkv, sm_scale, window, out=None):
+        """As verify_attn, each draft seeing only the last `window` keys up to itself."""
+        B, T_max, Hq, D = q.shape
+        num_pages, _, P, _ = k_pool.shape
+        if out is None:
+            out = np.full(q.shape, np.nan, dtype=np.float64)
+        rc = self.lib.splash_ref_verify_attn_window(
+            self._ptr(q), self._ptr(out), self._ptr(k_pool), self._ptr(v_pool),
+            self._ptr(k_scale), self._ptr(v_scale), self._ptr(block_table), block_table.shape[1],
+            self._ptr(context_lens), self._ptr(draft_lens), B, T_max, Hq, Hkv, D, P, num_pages,
+            float(sm_scale), int(window))
+        if rc:
+            raise ValueError(f"oracle verify_attn_window rejected its arguments (rc={rc})")
         return out
 
     def verify_attn_rows(self, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,

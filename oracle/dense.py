@@ -19,10 +19,11 @@ import numpy as np
 
 
 def dense_block_attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray,
-                          sm_scale: float, block_masks=None) -> np.ndarray:
+                          sm_scale: float, block_masks=None, window=None) -> np.ndarray:
     """q: [T][Hq][D]; k_hat, v_hat: [N][Hkv][D] (all fp64) -> out [T][Hq][D] fp64.
     block_masks: optional [T] integers; bit u of block_masks[t] lets draft t see
-    the key of draft u (a tree of candidates instead of the causal chain)."""
+    the key of draft u (a tree of candidates instead of the causal chain).
+    window: optional W >= 1; draft t at position p then sees only keys > p - W."""
     q = np.asarray(q, dtype=np.float64)
     k_hat = np.asarray(k_hat, dtype=np.float64)
     v_hat = np.asarray(v_hat, dtype=np.float64)
@@ -34,6 +35,8 @@ def dense_block_attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray,
     if block_masks is not None:                              # inside the block: the given bits
         bits = (np.asarray(block_masks, dtype=np.int64)[:, None] >> np.arange(T)[None, :]) & 1   # [T][T]
         hidden[:, N - T:] = bits == 0
+    if window is not None:                                   # sliding window: keys > p - W
+        hidden |= np.arange(N)[None, :] <= (visible_last - window)[:, None]
     out = np.empty((T, Hq, D))
     for h in range(Hq):
         g = h // group

@@ -218,6 +218,9 @@ int splash_ref_kv_append_int8(const void* k_new, const void* v_new, int src_dtyp
  * that verification checks at once, DFlash 2 section of the summary: several
  * candidate tokens per position), draft t sees every key before the block and
  * the block key of draft u exactly when bit u of *mask is set.
+ * With a window W > 0 (sliding-window attention, which the draft model uses
+ * so that its memory stays bounded at long context: summary, DFlash 2
+ * section), draft t sees only keys j > pos_t - W, on top of the rule above.
  * Writes the normalised row to out_row (D doubles) and returns the natural
  * log-sum-exp of the scaled scores; no visible key gives -inf and a zero row.
  */
@@ -234,10 +237,12 @@ static double attend_row(const uint16_t* q_row,
                          const uint16_t* k_scale, const uint16_t* v_scale,
                          const int32_t* bt_row, int b_ctx, int b_draft, int t, int g,
                          int Hkv, int D, int P, double sm_scale,
-                         int j_lo, int j_hi, const uint32_t* mask, double* z, double* out_row)
+                         int j_lo, int j_hi, const uint32_t* mask, int window, double* z, double* out_row)
 {
     int blk0 = b_ctx - b_draft;                 /* first key of the block     */
     int pos = blk0 + t;                         /* this draft's own position */
+    int j_base = j_lo;                          /* z is indexed from the range start */
+    if (window > 0 && pos - window + 1 > j_lo) j_lo = pos - window + 1;   /* keys j > pos - W */
     int end = mask ? (b_ctx < j_hi ? b_ctx : j_hi)
                    : (pos + 1 < j_hi ? pos + 1 : j_hi);   /* causal: keys 0..pos */
     for (int d = 0; d < D; ++d) out_row[d] = 0.0;
@@ -256,15 +261,15 @@ static double attend_row(const uint16_t* q_row,
             double kh = ks * (double)k_pool[k_index(page, g, slot, d, Hkv, P, D)];
             dot += (double)bf16_to_f32(q_row[d]) * kh;
         }
-        z[j - j_lo] = sm_scale * dot;
-        if (z[j - j_lo] > zmax) zmax = z[j - j_lo];
+        z[j - j_base] = sm_scale * dot;
+        if (z[j - j_base] > zmax) zmax = z[j - j_base];
     }
     /* softmax weights relative to the max, then the weighted sum of V_hat */
     double wsum = 0.0;
     for (int j = j_lo; j < end; ++j) {
         if (!key_visible(j, blk0, b_ctx, mask)) continue;
         int page = bt_row[j / P], slot = j % P;
-        double w = exp(z[j - j_lo] - zmax);
+        double w = exp(z[j - j_base] - zmax);
         double vs = (double)ref_f16_to_f32(v_scale[s_index(page, g, slot, Hkv, P)]);
         for (int d = 0; d < D; ++d)
             out_row[d] += w * (vs * (double)v_pool[v_index(page, g, slot, d, Hkv, P, D)]);
@@ -305,7 +310,7 @@ static int verify_attn_impl(const uint16_t* q, double* out,
                             const int32_t* block_table, int max_pages_per_seq,
                             const int32_t* context_lens, const int32_t* draft_lens,
                             int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
-                            double sm_scale, const uint32_t* block_masks)
+                            double sm_scale, const uint32_t* block_masks, int window)
 {
     int rc = check_attn_args(q, out, k_pool, v_pool, k_scale, v_scale, block_table,
                              context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages,
@@ -332,7 +337,7 @@ static int verify_attn_impl(const uint16_t* q, double* out,
                    block_table + (size_t)b * max_pages_per_seq,
                    context_lens[b], draft_lens[b], t, h / group, Hkv, D, P, sm_scale,
                    0, context_lens[b], block_masks ? block_masks + (size_t)b * T_max + t : NULL,
-                   z, out + row);
+                   window, z, out + row);
     }
     free(z);
     }
@@ -348,7 +353,7 @@ int splash_ref_verify_attn(const uint16_t* q, double* out,
                            double sm_scale)
 {
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
-                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale, NULL);
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale, NULL, 0);
 }
 
 int splash_ref_verify_attn_masked(const uint16_t* q, double* out,
@@ -362,7 +367,23 @@ int splash_ref_verify_attn_masked(const uint16_t* q, double* out,
     if (!block_masks || T_max > 32) return REF_ERR_ARG;
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale,
-                            block_masks);
+                            block_masks, 0);
+}
+
+/* splash_ref_verify_attn_window: causal block attention where draft t at
+ * position pos_t sees only keys pos_t - window < j <= pos_t (window >= 1). */
+int splash_ref_verify_attn_window(const uint16_t* q, double* out,
+                                  const int8_t* k_pool, const int8_t* v_pool,
+                                  const uint16_t* k_scale, const uint16_t* v_scale,
+                                  const int32_t* block_table, int max_pages_per_seq,
+                                  const int32_t* context_lens, const int32_t* draft_lens,
+                                  int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                                  double sm_scale, int window)
+{
+    if (window < 1) return REF_ERR_ARG;
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale,
+                            NULL, window);
 }
 
 /*
@@ -404,7 +425,7 @@ int splash_ref_verify_attn_rows(const uint16_t* q,
         attend_row(q + row, k_pool, v_pool, k_scale, v_scale,
                    block_table + (size_t)b * max_pages_per_seq,
                    context_lens[b], draft_lens[b], t, h / group, Hkv, D, P, sm_scale,
-                   0, context_lens[b], NULL, z, out_rows + (size_t)i * D);
+                   0, context_lens[b], NULL, 0, z, out_rows + (size_t)i * D);
     }
     free(z);
     }
@@ -458,7 +479,7 @@ int splash_ref_verify_attn_split(const uint16_t* q,
         part_lse[prow] = attend_row(q + qrow, k_pool, v_pool, k_scale, v_scale,
                                     block_table + (size_t)b * max_pages_per_seq,
                                     context_lens[b], draft_lens[b], t, h / group, Hkv, D, P,
-                                    sm_scale, (int)lo, (int)hi, NULL, z, part_o + prow * D);
+                                    sm_scale, (int)lo, (int)hi, NULL, 0, z, part_o + prow * D);
     }
     free(z);
     }

@@ -22,6 +22,9 @@ pins come from the mathematics and from library routines):
                          split, shift invariance)
   tree masks             the dense brute force with the same mask; the chain
                          mask bit-identical to the causal block
+  sliding windows        the dense brute force with the same window; W = 1
+                         gives each draft its own V row; a window past the
+                         context is the causal block, bit for bit
   acceptance             spiked logits with known greedy tokens (planted
                          acceptance points, no block, whole block kept); ties
                          to the lowest id, signed zeros, negatives; brute-force
@@ -549,6 +552,41 @@ def pin_tree_mask_chain_is_causal(orc, seed=32):
 
 
 # --------------------------------------------------------------------------
+# sliding-window masks
+# --------------------------------------------------------------------------
+def pin_window_dense(orc, seed=35):
+    """Windows from 1 key to past the context against the dense brute force."""
+    wl = _small_direct(seed, context_lens=[37, 50], draft_lens=[3, 5])
+    for W in (1, 2, 7, 16, 45, 200):
+        out = orc.verify_attn_window(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                                     wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale, W)
+        for b in range(wl.B):
+            k_hat, v_hat = dense_from_direct(wl, b)
+            d = int(wl.draft_lens[b])
+            ref = dense_block_attention(bf16_value(wl.q[b, :d]), k_hat, v_hat, wl.sm_scale, window=W)
+            assert rel_err(out[b, :d], ref) <= 1e-12, (W, rel_err(out[b, :d], ref))
+
+
+def pin_window_closed_forms(orc, seed=36):
+    """W = 1: each draft sees only its own key, so its row is that key's V-hat
+    (for every query); W at least the context: the causal block, bit for bit."""
+    wl = _small_direct(seed, context_lens=[37, 50], draft_lens=[3, 5])
+    one = orc.verify_attn_window(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                                 wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale, 1)
+    for b in range(wl.B):
+        _, v_hat = dense_from_direct(wl, b)
+        n, d = int(wl.context_lens[b]), int(wl.draft_lens[b])
+        for t in range(d):
+            for h in range(wl.Hq):
+                assert np.allclose(one[b, t, h], v_hat[n - d + t, h // (wl.Hq // wl.Hkv)], rtol=0, atol=1e-15)
+    causal = orc.verify_attn(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                             wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale)
+    wide = orc.verify_attn_window(wl.q, wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale, wl.block_table,
+                                  wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale, 50)
+    assert np.array_equal(causal, wide, equal_nan=True)
+
+
+# --------------------------------------------------------------------------
 # acceptance of a verified block
 # --------------------------------------------------------------------------
 def _check_planted(orc, case):
@@ -651,6 +689,8 @@ ALL_PINS = [
     pin_merge_closed_forms,
     pin_tree_mask_dense,
     pin_tree_mask_chain_is_causal,
+    pin_window_dense,
+    pin_window_closed_forms,
     pin_accept_planted,
     pin_accept_ties_lowest_id,
     pin_accept_equals_greedy_decoding,

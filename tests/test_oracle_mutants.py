@@ -56,6 +56,10 @@ MUTANTS = {
     "tree_mask_ignored": ("    if (!mask) return 1;", "    return 1;"),
     "tree_mask_bit_shift": ("return (int)((*mask >> (j - blk0)) & 1u);", "return (int)((*mask >> (j - blk0 + 1)) & 1u);"),
     "tree_mask_hides_context": ("    if (j < blk0) return 1;", "    if (j < blk0) return j + 1 < blk0;"),
+    # sliding windows
+    "window_off_by_one": ("if (window > 0 && pos - window + 1 > j_lo) j_lo = pos - window + 1;",
+                          "if (window > 0 && pos - window > j_lo) j_lo = pos - window;"),
+    "window_ignored": ("if (window > 0 && pos - window + 1 > j_lo) j_lo = pos - window + 1;", ""),
     # acceptance
     "accept_ties_highest": ("if (x > bv) { bv = x; best = v; }", "if (x >= bv) { bv = x; best = v; }"),
     "accept_compares_bits": ("float x = bf16_to_f32(row[v]);", "float x = (float)row[v];"),
