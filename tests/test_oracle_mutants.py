@@ -38,7 +38,7 @@ MUTANTS = {
     # attention
     "causal_excludes_self": (": (pos + 1 < j_hi ? pos + 1 : j_hi);", ": (pos < j_hi ? pos : j_hi);"),
     "causal_sees_next": (": (pos + 1 < j_hi ? pos + 1 : j_hi);", ": (pos + 2 < j_hi ? pos + 2 : j_hi);"),
-    "no_sm_scale": ("z[j - j_lo] = sm_scale * dot;", "z[j - j_lo] = dot;"),
+    "no_sm_scale": ("z[j - j_base] = sm_scale * dot;", "z[j - j_base] = dot;"),
     "k_uses_v_scale": ("double ks = (double)ref_f16_to_f32(k_scale[",
                        "double ks = (double)ref_f16_to_f32(v_scale["),
     "v_uses_k_scale": ("double vs = (double)ref_f16_to_f32(v_scale[",
