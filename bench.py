@@ -194,6 +194,13 @@ def main():
         sda.splash_verify_attn_masked(q, out, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t, tree, ctx,
                                       wl.sm_scale, num_splits=S_req, workspace=ws)
 
+    # the same call for a sliding-window drafter: only the last W keys per draft
+    W = 4096
+
+    def verify_window(r):
+        sda.splash_verify_attn_window(q, out, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t, W, ctx,
+                                      wl.sm_scale, workspace=ws)
+
     def partition(r):
         sda.splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, bts[r], ctx_t, dl_t,
                                          ctx, wl.sm_scale, S, part_o, part_lse)
@@ -207,7 +214,9 @@ def main():
     C = max(d for d in range(1, R + 1) if args.steps % d == 0)
     graphs = {}
     verify_tree(0)
-    for name, fn in (("step", step), ("verify", verify), ("verify_tree", verify_tree)):
+    verify_window(0)
+    for name, fn in (("step", step), ("verify", verify), ("verify_tree", verify_tree),
+                     ("verify_window", verify_window)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             for r in range(C):
@@ -238,6 +247,8 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     us_verify = timed_replays(graphs["verify"], args.steps, args.warmup) * 1e3
     us_tree = timed_replays(graphs["verify_tree"], args.steps, args.warmup) * 1e3
+    us_window = timed_replays(graphs["verify_window"], args.steps, args.warmup) * 1e3
+    window_bytes = verify_bytes(min(ctx, W + T - 1), Hkv, D, T, Hq)
 
     # the partition kernel alone, launched back to back on its stream: one event
     # pair brackets the launches (queued behind a sleep, so the host's launch
@@ -309,6 +320,8 @@ def main():
                    "splits": S, "replicas": R, "calls_per_graph": C, "step_bytes": step_bytes,
                    "verify_us_per_call": round(us_verify, 2),
                    "verify_tree_mask_us_per_call": round(us_tree, 2),
+                   "verify_window_4096": {"us_per_call": round(us_window, 2),
+                                          "gbs": round(window_bytes / (us_window * 1e-6) / 1e9, 1)},
                    "partition_us_mall_warm": round(part_us_warm, 3),
                    "hbm_read_ceiling_pages_gbs": round(stream_gbs, 1),
                    "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)},

@@ -191,6 +191,38 @@ int splash_verify_attn_masked(const uint16_t* q, uint16_t* out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * splash_verify_attn_window -- splash_verify_attn where every draft sees only
+ * the last `window` keys up to and including itself: draft t at position
+ * p = context_lens[b] - draft_lens[b] + t attends to keys p - window < j <= p.
+ * Sliding-window attention is what the draft model uses so that its memory
+ * stays bounded however long the context grows (discuss.pytorch.kr summary,
+ * DFlash 2 section).  Only the pages inside a request's window are read: the
+ * splits cover splash_verify_attn_window_tokens(max_context_len, T_max,
+ * window, P) tokens, so size the workspace with
+ * splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S) for the S that
+ * splash_verify_attn_default_splits (or num_splits) gives over that span.
+ * window >= 1 (else SPLASH_ERR_INVALID_ARGUMENT); a window of at least the
+ * context gives splash_verify_attn's result.  Everything else as
+ * splash_verify_attn.
+ */
+int splash_verify_attn_window(const uint16_t* q, uint16_t* out,
+                              const int8_t* k_pool, const int8_t* v_pool,
+                              const uint16_t* k_scale, const uint16_t* v_scale,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* context_lens, const int32_t* draft_lens,
+                              int window,
+                              int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                              int max_context_len, float sm_scale, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * splash_verify_attn_window_tokens -- the token span the splits of a windowed
+ * call cover: min(max_context_len, P * (ceil((T_max + window - 1) / P) + 1)).
+ * Negative status on bad arguments.
+ */
+int splash_verify_attn_window_tokens(int max_context_len, int T_max, int window, int P);
+
+/*
  * splash_verify_attn_partition -- the first half of splash_verify_attn on its
  * own: for each context split s (pages [s*L, (s+1)*L) with
  * L = splash_verify_attn_split_pages(...)), write for draft t < draft_lens[b]

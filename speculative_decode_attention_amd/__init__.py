@@ -33,6 +33,8 @@ EXPORTED = (
     "splash_verify_attn_workspace_bytes",
     "splash_verify_attn",
     "splash_verify_attn_masked",
+    "splash_verify_attn_window",
+    "splash_verify_attn_window_tokens",
     "splash_verify_attn_partition",
     "splash_verify_attn_split_pages",
     "splash_verify_attn_splitk_merge",
@@ -72,6 +74,9 @@ def load_library(path: Path | None = None):
                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
     lib.splash_verify_attn_masked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                                               _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_verify_attn_window.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I,
+                                              _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_verify_attn_window_tokens.argtypes = [_I, _I, _I, _I]
     lib.splash_verify_attn_partition.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                  _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
     lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
@@ -231,8 +236,23 @@ def splash_verify_attn_masked(q, out, k_pool, v_pool, k_scale, v_scale, block_ta
                    max_context_len, sm_scale, num_splits, workspace, stream, block_masks)
 
 
+def splash_verify_attn_window_tokens(max_context_len, T_max, window, P=PAGE_SIZE):
+    n = int(_lib().splash_verify_attn_window_tokens(int(max_context_len), int(T_max), int(window), int(P)))
+    if n < 0:
+        raise SplashError(-n, "splash_verify_attn_window_tokens")
+    return n
+
+
+def splash_verify_attn_window(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                              draft_lens, window, max_context_len, sm_scale, num_splits=0,
+                              workspace=None, stream=None):
+    """splash_verify_attn where each draft sees only the last `window` keys up to itself."""
+    return _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
+                   max_context_len, sm_scale, num_splits, workspace, stream, None, int(window))
+
+
 def _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
-            max_context_len, sm_scale, num_splits, workspace, stream, block_masks):
+            max_context_len, sm_scale, num_splits, workspace, stream, block_masks, window=0):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B][T_max][Hq][D]")
@@ -243,9 +263,11 @@ def _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
     if Dq != D:
         raise ValueError("q head dim does not match the pools")
     maxp = _lens(block_table, context_lens, draft_lens, B)
+    span = (splash_verify_attn_window_tokens(max_context_len, T_max, window, P)
+            if window and max_context_len else max_context_len)
     S_req = num_splits if num_splits > 0 else (
-        splash_verify_attn_default_splits(B, Hkv, max_context_len, P, D) if B and max_context_len else 1)
-    S = effective_splits(max_context_len, P, S_req)
+        splash_verify_attn_default_splits(B, Hkv, span, P, D) if B and span else 1)
+    S = effective_splits(span, P, S_req) if span else 1
     need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S)
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -253,7 +275,14 @@ def _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         _dev(workspace, "workspace", (torch.uint8, torch.int8, torch.float32))
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    if block_masks is None:
+    if window:
+        rc = _lib().splash_verify_attn_window(
+            q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+            v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),
+            draft_lens.data_ptr(), int(window), B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len),
+            float(sm_scale), int(S_req), ws_ptr, ws_bytes, _stream(stream))
+        _check(rc, "splash_verify_attn_window")
+    elif block_masks is None:
         rc = _lib().splash_verify_attn(
             q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
             v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),

@@ -138,23 +138,28 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
                             int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
                             int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
                             int max_context_len, float sm_scale, int num_splits, void* workspace,
-                            size_t workspace_bytes, void* stream, const uint32_t* block_masks) {
+                            size_t workspace_bytes, void* stream, const uint32_t* block_masks,
+                            int window) {
     int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                                  draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
                                  max_context_len, sm_scale);
     if (rc != SPLASH_OK) return rc;
     if (!out || !aligned16(out) || num_splits < 0) return SPLASH_ERR_INVALID_ARGUMENT;
     if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;   // no draft row can exist
+    // the tokens the splits cover: the whole context, or what a window leaves of it
+    const int span = window > 0 ? splash_verify_attn_window_tokens(max_context_len, T_max, window, P)
+                                : max_context_len;
     if (num_splits == 0) {
-        num_splits = splash_verify_attn_default_splits(B, Hkv, max_context_len, P, D);
+        num_splits = splash_verify_attn_default_splits(B, Hkv, span, P, D);
         if (num_splits < 0) return -num_splits;
     }
-    const int L = pages_per_split(max_context_len, P, num_splits);
-    const int S = ceil_div(ceil_div(max_context_len, P), L);     // splits that hold pages
+    const int L = pages_per_split(span, P, num_splits);
+    const int S = ceil_div(ceil_div(span, P), L);                // splits that hold pages
     VerifyArgs a{q, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, block_table,
                  max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale, S, L,
                  num_pages};
     a.block_masks = block_masks;
+    a.window = window;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (S == 1) {
         a.out = out;
@@ -179,7 +184,7 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
                        size_t workspace_bytes, void* stream) {
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
-                            sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr);
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 int splash_verify_attn_masked(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
@@ -191,7 +196,27 @@ int splash_verify_attn_masked(const uint16_t* q, uint16_t* out, const int8_t* k_
     if (!block_masks) return SPLASH_ERR_INVALID_ARGUMENT;
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
-                            sm_scale, num_splits, workspace, workspace_bytes, stream, block_masks);
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, block_masks, 0);
+}
+
+int splash_verify_attn_window_tokens(int max_context_len, int T_max, int window, int P) {
+    if (max_context_len < 0 || T_max < 0 || window < 1 || P <= 0) return -SPLASH_ERR_INVALID_ARGUMENT;
+    // keys the block's drafts can see start at ctx - d + 1 - window, which may sit
+    // inside a page: at most ceil((d + window - 1) / P) + 1 pages per request
+    const long bound = (long)P * (ceil_div(T_max + window - 1, P) + 1);
+    return bound < max_context_len ? (int)bound : max_context_len;
+}
+
+int splash_verify_attn_window(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                              const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                              int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
+                              int window, int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                              int max_context_len, float sm_scale, int num_splits, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (window < 1) return SPLASH_ERR_INVALID_ARGUMENT;
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr, window);
 }
 
 int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,

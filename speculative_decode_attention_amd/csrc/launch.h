@@ -42,6 +42,7 @@ struct VerifyArgs {
     int pages_per_split;       // L, a multiple of kPagesPerIter
     int num_pages;             // pool size; page ids are clamped into [0, num_pages)
     const uint32_t* block_masks = nullptr;   // [B][T_max] bit u of row t: draft t sees draft u; null: causal
+    int window = 0;                          // > 0: draft at position p sees keys p - window < j <= p
 };
 
 struct TiledMergeArgs {

@@ -61,6 +61,9 @@ constexpr int kRing = 4;       // K and V rings, in steps
 constexpr int kKAhead = 3;     // K(i + 3) is issued at step i
 constexpr int kIdAhead = 7;    // the page id of step i + 7 is copied at step i
 constexpr int kIdRing = 8;
+// how a draft sees the block and the context: the causal chain, a tree of
+// candidates (per-draft bit masks), or a sliding window over the keys
+constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -210,7 +213,7 @@ __device__ __forceinline__ int k_swizzle(int slot) {
 //  * Output wave c = v - 4: copies page c of every step (K rows, scales, page
 //    id, V rows) and owns columns [32 c SPW, 32 (c + 1) SPW) of all rows for
 //    P V, so every V code is converted once.
-template <int D, int G, int NTU, bool MASKED>
+template <int D, int G, int NTU, int MASK>
 __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds, const int b, const int g,
                                                const int s, const int dl, const int ctx, const int pg_begin,
                                                const int pg_end) {
@@ -321,7 +324,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         if (lane < kIdAhead) *reinterpret_cast<int*>(lds + C::ID_OFF + (lane * kPagesPerIter + c) * 4) = ids0;
         if (c == 0 && lane < 2 * kWaves / 4)                  // both flag buffers start clear
             *reinterpret_cast<uint32_t*>(lds + C::F_OFF + 4 * lane) = 0u;
-        if (MASKED && c == 1 && lane < 16)                    // the drafts' block masks
+        if (MASK == kMaskTree && c == 1 && lane < 16)         // the drafts' block masks
             *reinterpret_cast<uint32_t*>(lds + C::MASK_OFF + 4 * lane) =
                 lane < a.T_max ? a.block_masks[(size_t)b * a.T_max + lane] : 0u;
 #pragma unroll
@@ -536,7 +539,8 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 vsh[k][1] = bit_cast<f16x2_t>(vs[1]);
                 const int key0 = (pg_begin + kPagesPerIter * it + p) * kPage;
                 // every key of the page is visible to every row (padded rows see q = 0)
-                const bool masked = may_mask && !(key0 + kPage - 1 <= ctx - dl);
+                bool masked = may_mask && !(key0 + kPage - 1 <= ctx - dl);
+                if constexpr (MASK == kMaskWindow) masked = may_mask && !(key0 + kPage - 1 <= ctx - dl && key0 >= ctx - a.window);
                 const int kl = key0 + 4 * gq;
                 if (masked) {                                 // keys past the context carry no V weight
 #pragma unroll
@@ -561,7 +565,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                         // draft u when bit u of its mask is set (the causal chain:
                         // bits 0..t); a padded row sees nothing here
                         const int row = 16 * (t0 + i) + li;
-                        if constexpr (MASKED) {
+                        if constexpr (MASK == kMaskTree) {
                             const int blk0 = ctx - dl;
                             const uint32_t mrow = row < rows ? *reinterpret_cast<const uint32_t*>(lds + C::MASK_OFF + 4 * (row / G)) : 0u;
 #pragma unroll
@@ -571,6 +575,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                                 const bool vis = (row < rows) & ((key < blk0) | (inblk & (((mrow >> (u & 31)) & 1u) != 0u)));
                                 zs[k][i][j] = vis ? zs[k][i][j] : -INFINITY;
                             }
+                        } else if constexpr (MASK == kMaskWindow) {
+                            // keys pos - W < key <= pos of the row's own position pos
+                            const int pos = row < rows ? ctx - dl + row / G : -1;   // -1: padded row
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                zs[k][i][j] = (kl + j <= pos) & (kl + j > pos - a.window) ? zs[k][i][j] : -INFINITY;
                         } else {
                             const int last_key = row < rows ? ctx - dl + row / G : -1;   // -1: padded row
 #pragma unroll
@@ -592,7 +602,10 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             // as one block: the K reads go first, so their latency overlaps the
             // softmax, and the two pages' MFMA chains interleave.
             const int key_end = (pg_begin + kPagesPerIter * it + 2 * pp + 2) * kPage;   // one past page 2 pp + 1
-            if (do_sm && it < n && it <= lv1 && key_end - 1 <= ctx - dl) {
+            bool steady = do_sm && it < n && it <= lv1 && key_end - 1 <= ctx - dl;
+            if constexpr (MASK == kMaskWindow)              // every row sees the step's first key
+                steady = steady && (pg_begin + kPagesPerIter * it + 2 * pp) * kPage >= ctx - a.window;
+            if (steady) {
                 u32x4_t kraw[2][KB / 2];
                 u32x2_t ks[2], vs[2];
                 read_k(0, kraw[0], ks[0], vs[0]);
@@ -815,19 +828,19 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 }
 
 // run the body with the number of row tiles in use as a compile-time constant
-template <int D, int G, int NTU, bool MASKED>
+template <int D, int G, int NTU, int MASK>
 __device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a, uint8_t* lds, int b, int g,
                                                int s, int dl, int ctx, int pg_begin, int pg_end) {
     if constexpr (NTU > 1) {
         if (nt_used < NTU) {
-            dispatch_tiles<D, G, NTU - 1, MASKED>(nt_used, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+            dispatch_tiles<D, G, NTU - 1, MASK>(nt_used, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
             return;
         }
     }
-    partition_body<D, G, NTU, MASKED>(a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+    partition_body<D, G, NTU, MASK>(a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
 }
 
-template <int D, int G, bool MASKED>
+template <int D, int G, int MASK>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void verify_partition_kernel(const VerifyArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg<D, G>::TOTAL];
@@ -844,7 +857,9 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int ctx = a.context_lens[b];                        // both loads in flight together
     if (dl <= 0) return;                                      // request is a no-op
     const int n_pages = (ctx + kPage - 1) / kPage;
-    const int pg_begin = s * a.pages_per_split;
+    // a window hides every key before the first one the block's first draft sees
+    const int lo_page = MASK == kMaskWindow ? max(0, ctx - dl + 1 - a.window) / kPage : 0;
+    const int pg_begin = lo_page + s * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_pages);
     const int rows = G * dl;
     if (pg_begin >= pg_end) {                                 // empty split: mark it, write no row
@@ -853,7 +868,7 @@ void verify_partition_kernel(const VerifyArgs a) {
         }
         return;
     }
-    dispatch_tiles<D, G, G, MASKED>((rows + 15) >> 4, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+    dispatch_tiles<D, G, G, MASK>((rows + 15) >> 4, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
 }
 
 // ---------------------------------------------------------------------------
@@ -983,9 +998,11 @@ static hipError_t launch_partition_dg(const VerifyArgs& a, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (a.block_masks != nullptr)
-        hipLaunchKernelGGL((verify_partition_kernel<D, G, true>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskTree>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+    else if (a.window > 0)
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskWindow>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((verify_partition_kernel<D, G, false>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskCausal>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
