@@ -53,6 +53,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0                            # dense fp16/bf16 MFMA, MI355X
 METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak) at 32K ctx, T=16"
 WORKLOAD = "verify 1 req x ctx 32768, T=16 drafts, 24q/4kv heads, D=256, int8 KV in 16-token pages"
 PART_KERNEL = "verify_partition_kernel"
@@ -285,6 +286,7 @@ def main():
     # permuted positions of a 4 GiB pool, 16-byte direct-to-LDS loads, no compute
     stream_gbs = read_ceiling_gbs(dev)
     accept = accept_leg(dev, args.steps)
+    prefill = prefill_leg(dev, args.steps)
     part_bytes = verify_bytes(ctx, Hkv, D, T, Hq)
     achieved = part_bytes / (part_us * 1e-6) / 1e9
 
@@ -335,6 +337,7 @@ def main():
                      "frac_of_page_read_ceiling": round(achieved / stream_gbs, 4)},
         "cpu_baseline": cpu,
         "accept": accept,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 
@@ -383,6 +386,59 @@ def accept_leg(dev, steps: int) -> dict:
                      "us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
         del logits, base
     return res
+
+
+def prefill_leg(dev, steps: int) -> dict:
+    """Chunked prefill on the same cache layout: a 512-token chunk closing a
+    32,768-token context (24 q / 4 kv heads, D = 256), its K/V already appended.
+    FLOPs count QK^T and PV over each token's visible keys (4 * D per key and
+    q head); bytes are the distinct K/V pages and scales of the context plus
+    the chunk's q and out, each read or written once."""
+    import torch
+    import speculative_decode_attention_amd as sda
+    from speculative_decode_attention_amd import synth
+    ctx, chunk, Hq, Hkv, D, P = 32768, 512, 24, 4, 256, 16
+    wl = synth.make_workload("prefill", 31, B=1, context_lens=[ctx], T_max=chunk, draft_lens=[chunk],
+                             Hq=Hq, Hkv=Hkv, D=D, num_pages=ctx // P + 8)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    pools = [up(a) for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+    for ph in wl.appends:
+        sda.splash_kv_append_int8(up(ph.k_src), up(ph.v_src), *pools, up(ph.block_table),
+                                  up(ph.context_lens), up(ph.draft_lens))
+    q, bt, cl, dl = up(wl.q), up(wl.block_table), up(wl.context_lens), up(wl.draft_lens)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(sda.splash_prefill_attn_workspace_bytes(1, chunk, Hq, Hkv, D, ctx), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        sda.splash_prefill_attn(q, out, *pools, bt, cl, dl, ctx, wl.sm_scale, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    n = max(steps // 10, 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(n * 60e-6 * 2.0e9))
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    keys = sum(ctx - chunk + t + 1 for t in range(chunk))
+    flops = 4 * D * Hq * keys
+    kv_bytes = verify_bytes(ctx, Hkv, D, chunk, Hq)
+    del pools, q, out, ws
+    return {"workload": "512-token chunk at the end of a 32768-token context", "chunk": chunk,
+            "context": ctx, "us_per_call": round(us, 1), "flops": flops,
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "frac_of_fp16_mfma_peak": round(flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "distinct_bytes": kv_bytes, "distinct_gbs": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+            "tokens_per_s": round(chunk / (us * 1e-6), 0)}
 
 
 def read_ceiling_gbs(dev) -> float:

@@ -223,6 +223,34 @@ int splash_verify_attn_window(const uint16_t* q, uint16_t* out,
 int splash_verify_attn_window_tokens(int max_context_len, int T_max, int window, int P);
 
 /*
+ * splash_prefill_attn -- attention for a chunk of prefill tokens over the same
+ * int8 paged cache.  The engine keeps a separate attention kernel for prefill
+ * (large blocks) next to the verify one (discuss.pytorch.kr summary, section
+ * "Metal kernels generated to shape"); the computation is the verify
+ * definition with a long block: chunk token t < chunk_lens[b] of request b sits
+ * at position p = context_lens[b] - chunk_lens[b] + t and attends to keys
+ * 0..p.  The chunk's K and V must already be appended.  T_max is any length
+ * (B * ceil(T_max / 16) <= 65535); q and out are bf16 [B][T_max][Hq][D]; rows
+ * t >= chunk_lens[b] are left untouched.  The chunk runs as ceil(T_max / 16)
+ * verify blocks of 16 tokens per request in one launch of each kernel, every
+ * block attending over the cache up to its own last token (the pages a block
+ * reads are read again by the later blocks of the chunk; the Infinity Cache
+ * serves most of the repeats).  workspace: splash_prefill_attn_workspace_bytes
+ * bytes for the same arguments (0: none needed).  Everything else as
+ * splash_verify_attn; chunk_lens plays the part of draft_lens.
+ */
+int splash_prefill_attn(const uint16_t* q, uint16_t* out,
+                        const int8_t* k_pool, const int8_t* v_pool,
+                        const uint16_t* k_scale, const uint16_t* v_scale,
+                        const int32_t* block_table, int max_pages_per_seq,
+                        const int32_t* context_lens, const int32_t* chunk_lens,
+                        int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                        int max_context_len, float sm_scale, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+size_t splash_prefill_attn_workspace_bytes(int B, int T_max, int Hq, int Hkv, int D, int P,
+                                           int max_context_len, int num_splits);
+
+/*
  * splash_verify_attn_partition -- the first half of splash_verify_attn on its
  * own: for each context split s (pages [s*L, (s+1)*L) with
  * L = splash_verify_attn_split_pages(...)), write for draft t < draft_lens[b]

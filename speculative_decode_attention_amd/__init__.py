@@ -35,6 +35,8 @@ EXPORTED = (
     "splash_verify_attn_masked",
     "splash_verify_attn_window",
     "splash_verify_attn_window_tokens",
+    "splash_prefill_attn",
+    "splash_prefill_attn_workspace_bytes",
     "splash_verify_attn_partition",
     "splash_verify_attn_split_pages",
     "splash_verify_attn_splitk_merge",
@@ -77,6 +79,10 @@ def load_library(path: Path | None = None):
     lib.splash_verify_attn_window.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I,
                                               _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
     lib.splash_verify_attn_window_tokens.argtypes = [_I, _I, _I, _I]
+    lib.splash_prefill_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_prefill_attn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I]
+    lib.splash_prefill_attn_workspace_bytes.restype = _Z
     lib.splash_verify_attn_partition.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                  _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
     lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
@@ -88,7 +94,7 @@ def load_library(path: Path | None = None):
     lib.splash_status_string.restype = ctypes.c_char_p
     for name in EXPORTED:
         if name not in ("splash_verify_attn_workspace_bytes", "splash_verify_accept_workspace_bytes",
-                        "splash_status_string"):
+                        "splash_prefill_attn_workspace_bytes", "splash_status_string"):
             getattr(lib, name).restype = _I
     if path is None:
         _lib_handle = lib
@@ -377,3 +383,38 @@ def splash_verify_accept(logits, block_tokens, draft_lens, context_lens, accepte
                                      B, T_max, V, workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(rc, "splash_verify_accept")
     return accepted, next_token
+
+
+def splash_prefill_attn_workspace_bytes(B, T_max, Hq, Hkv, D, max_context_len, num_splits=0, P=PAGE_SIZE):
+    return int(_lib().splash_prefill_attn_workspace_bytes(int(B), int(T_max), int(Hq), int(Hkv), int(D), int(P),
+                                                           int(max_context_len), int(num_splits)))
+
+
+def splash_prefill_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, chunk_lens,
+                        max_context_len, sm_scale, num_splits=0, workspace=None, stream=None):
+    """Causal attention of a prefill chunk over the int8 paged cache (the chunk's
+    K/V already appended); writes out[b][t][h][:] for t < chunk_lens[b]."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B][T_max][Hq][D]")
+    B, T_max, Hq, Dq = (int(x) for x in q.shape)
+    _dev(q, "q", (torch.bfloat16, torch.int16))
+    _dev(out, "out", (torch.bfloat16, torch.int16), tuple(q.shape))
+    num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
+    if Dq != D:
+        raise ValueError("q head dim does not match the pools")
+    maxp = _lens(block_table, context_lens, chunk_lens, B)
+    need = splash_prefill_attn_workspace_bytes(B, T_max, Hq, Hkv, D, max_context_len, num_splits, P)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _dev(workspace, "workspace", (torch.uint8, torch.int8, torch.float32))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = _lib().splash_prefill_attn(
+        q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(), chunk_lens.data_ptr(),
+        B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len), float(sm_scale), int(num_splits),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "splash_prefill_attn")
+    return out

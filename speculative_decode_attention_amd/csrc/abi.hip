@@ -139,40 +139,46 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
                             int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
                             int max_context_len, float sm_scale, int num_splits, void* workspace,
                             size_t workspace_bytes, void* stream, const uint32_t* block_masks,
-                            int window) {
+                            int window, bool prefill = false) {
+    // a prefill chunk runs as ceil(T_max / 16) verify blocks per request
+    const int nblk = prefill ? ceil_div(T_max, kMaxVerifyT) : 1;
+    if (prefill && (T_max < 0 || (long)B * nblk > 65535)) return SPLASH_ERR_INVALID_ARGUMENT;
     int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
-                                 draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
-                                 max_context_len, sm_scale);
+                                 draft_lens, max_pages_per_seq, B, prefill ? (T_max < kMaxVerifyT ? T_max : kMaxVerifyT) : T_max,
+                                 Hq, Hkv, D, P, num_pages, max_context_len, sm_scale);
     if (rc != SPLASH_OK) return rc;
     if (!out || !aligned16(out) || num_splits < 0) return SPLASH_ERR_INVALID_ARGUMENT;
     if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;   // no draft row can exist
     // the tokens the splits cover: the whole context, or what a window leaves of it
     const int span = window > 0 ? splash_verify_attn_window_tokens(max_context_len, T_max, window, P)
                                 : max_context_len;
+    const int items = B * nblk;                                  // requests, or 16-token blocks of chunks
     if (num_splits == 0) {
-        num_splits = splash_verify_attn_default_splits(B, Hkv, span, P, D);
+        num_splits = splash_verify_attn_default_splits(items, Hkv, span, P, D);
         if (num_splits < 0) return -num_splits;
     }
     const int L = pages_per_split(span, P, num_splits);
     const int S = ceil_div(ceil_div(span, P), L);                // splits that hold pages
     VerifyArgs a{q, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, block_table,
-                 max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale, S, L,
+                 max_pages_per_seq, context_lens, draft_lens, items, T_max, Hq, Hkv, D, sm_scale, S, L,
                  num_pages};
     a.block_masks = block_masks;
     a.window = window;
+    a.blocks_per_req = nblk;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (S == 1) {
         a.out = out;
         return launch_verify_partition(a, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
     }
-    const size_t need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S);
+    const size_t need = splash_verify_attn_workspace_bytes(items, prefill ? kMaxVerifyT : T_max, Hq, D, S);
     if (!workspace || !aligned16(workspace)) return SPLASH_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < need) return SPLASH_ERR_WORKSPACE_TOO_SMALL;
-    const size_t rows = (size_t)B * 16 * Hq * S;
+    const size_t rows = (size_t)items * 16 * Hq * S;
     a.part_h = static_cast<uint16_t*>(workspace);
     a.part_hlse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * D * 2, 256));
     if (launch_verify_partition(a, st) != hipSuccess) return SPLASH_ERR_LAUNCH;
-    TiledMergeArgs m{a.part_h, a.part_hlse, out, draft_lens, B, T_max, Hq, Hkv, D, S};
+    TiledMergeArgs m{a.part_h, a.part_hlse, out, draft_lens, items, T_max, Hq, Hkv, D, S};
+    m.blocks_per_req = nblk;
     return launch_splitk_merge_tiled(m, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
 }
 
@@ -197,6 +203,29 @@ int splash_verify_attn_masked(const uint16_t* q, uint16_t* out, const int8_t* k_
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
                             sm_scale, num_splits, workspace, workspace_bytes, stream, block_masks, 0);
+}
+
+size_t splash_prefill_attn_workspace_bytes(int B, int T_max, int Hq, int Hkv, int D, int P,
+                                           int max_context_len, int num_splits) {
+    if (B < 0 || T_max < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_context_len < 0 || num_splits < 0)
+        return 0;
+    if (B == 0 || T_max == 0 || max_context_len == 0) return 0;
+    const int items = B * ceil_div(T_max, kMaxVerifyT);
+    if (num_splits == 0) num_splits = splash_verify_attn_default_splits(items, Hkv, max_context_len, P, D);
+    if (num_splits <= 0) return 0;
+    const int L = pages_per_split(max_context_len, P, num_splits);
+    const int S = ceil_div(ceil_div(max_context_len, P), L);
+    return S == 1 ? 0 : splash_verify_attn_workspace_bytes(items, kMaxVerifyT, Hq, D, S);
+}
+
+int splash_prefill_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                        const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                        int max_pages_per_seq, const int32_t* context_lens, const int32_t* chunk_lens, int B,
+                        int T_max, int Hq, int Hkv, int D, int P, int num_pages, int max_context_len,
+                        float sm_scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, chunk_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr, 0, true);
 }
 
 int splash_verify_attn_window_tokens(int max_context_len, int T_max, int window, int P) {

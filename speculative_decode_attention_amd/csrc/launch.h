@@ -43,6 +43,7 @@ struct VerifyArgs {
     int num_pages;             // pool size; page ids are clamped into [0, num_pages)
     const uint32_t* block_masks = nullptr;   // [B][T_max] bit u of row t: draft t sees draft u; null: causal
     int window = 0;                          // > 0: draft at position p sees keys p - window < j <= p
+    int blocks_per_req = 1;                  // > 1: a prefill chunk cut into 16-token blocks, B counts blocks
 };
 
 struct TiledMergeArgs {
@@ -51,6 +52,7 @@ struct TiledMergeArgs {
     uint16_t* out;
     const int32_t* draft_lens;
     int B, T_max, Hq, Hkv, D, num_splits;
+    int blocks_per_req = 1;                  // as in VerifyArgs
 };
 
 

@@ -65,6 +65,24 @@ constexpr int kIdRing = 8;
 // candidates (per-draft bit masks), or a sliding window over the keys
 constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2;
 
+// A work item's request.  Verify: request b itself.  A prefill chunk of
+// n_b tokens is cut into blocks of 16 (blocks_per_req of them per request):
+// item b is block j of request br, its drafts are chunk tokens 16 j + t
+// (t < dl) and its context ends after them, so the block is exactly a verify
+// block over the cache up to its own last token.
+struct BlockReq {
+    int req, t_off, dl, ctx;
+};
+__device__ __forceinline__ BlockReq block_req(const int32_t* draft_lens, const int32_t* context_lens, int b,
+                                              int nblk) {
+    const int br = nblk == 1 ? b : b / nblk;
+    const int t_off = 16 * (b - br * nblk);
+    const int d_all = draft_lens[br];
+    const int ctx_all = context_lens != nullptr ? context_lens[br] : 0;
+    const int dl = nblk == 1 ? d_all : min(max(d_all - t_off, 0), 16);
+    return BlockReq{br, t_off, dl, ctx_all - (d_all - t_off - dl)};
+}
+
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -214,9 +232,9 @@ __device__ __forceinline__ int k_swizzle(int slot) {
 //    id, V rows) and owns columns [32 c SPW, 32 (c + 1) SPW) of all rows for
 //    P V, so every V code is converted once.
 template <int D, int G, int NTU, int MASK>
-__device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds, const int b, const int g,
-                                               const int s, const int dl, const int ctx, const int pg_begin,
-                                               const int pg_end) {
+__device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds, const int b, const int br,
+                                               const int t_off, const int g, const int s, const int dl,
+                                               const int ctx, const int pg_begin, const int pg_end) {
     using C = Cfg<D, G>;
     constexpr int KB = C::KB, NI = C::NI;
     constexpr int NH = (NTU + 1) / 2;                         // 16-row tiles per half
@@ -259,7 +277,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     // through the scalar cache (counted apart from the vector copies, so waiting
     // for them holds no copy back)
     const int c = v & 3;                                      // output wave: page and column quarter
-    const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq + pg_begin + c;   // + 4 j
+    const int32_t* bt = a.block_table + (size_t)br * a.max_pages_per_seq + pg_begin + c;   // + 4 j
     const int last_c = last_step(c);
     typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
     int idj[kIdAhead];
@@ -276,7 +294,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         if (row < rows) {
             const int lc = pc ^ (row % C::QSWZ);
             const int t = row / G, hq = g * G + row % G;
-            dma16_to_lds(a.q + (((size_t)b * a.T_max + t) * Hq + hq) * D + 8 * lc,
+            dma16_to_lds(a.q + (((size_t)br * a.T_max + t_off + t) * Hq + hq) * D + 8 * lc,
                          lds_base + C::Q_OFF + 1024 * (v + kWaves * k));
         }
     }
@@ -326,7 +344,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             *reinterpret_cast<uint32_t*>(lds + C::F_OFF + 4 * lane) = 0u;
         if (MASK == kMaskTree && c == 1 && lane < 16)         // the drafts' block masks
             *reinterpret_cast<uint32_t*>(lds + C::MASK_OFF + 4 * lane) =
-                lane < a.T_max ? a.block_masks[(size_t)b * a.T_max + lane] : 0u;
+                lane < a.T_max ? a.block_masks[(size_t)br * a.T_max + lane] : 0u;
 #pragma unroll
         for (int j = 0; j < kKAhead; ++j) issue_k(j, clamp_page(idj[j]));
         issue_v(0, clamp_page(idj[0]));
@@ -793,7 +811,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         for (int sl = 0; sl < SPW; ++sl) {
             const int vs = c * SPW + sl;                      // 32-column slice
             if (a.out != nullptr) {
-                uint16_t* orow = a.out + (((size_t)b * a.T_max + t) * Hq + hq) * D;
+                uint16_t* orow = a.out + (((size_t)br * a.T_max + t_off + t) * Hq + hq) * D;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int d = 32 * vs + 8 * q4 + 4 * (lane >> 5);
@@ -829,15 +847,15 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 
 // run the body with the number of row tiles in use as a compile-time constant
 template <int D, int G, int NTU, int MASK>
-__device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a, uint8_t* lds, int b, int g,
-                                               int s, int dl, int ctx, int pg_begin, int pg_end) {
+__device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a, uint8_t* lds, int b, int br,
+                                               int t_off, int g, int s, int dl, int ctx, int pg_begin, int pg_end) {
     if constexpr (NTU > 1) {
         if (nt_used < NTU) {
-            dispatch_tiles<D, G, NTU - 1, MASK>(nt_used, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+            dispatch_tiles<D, G, NTU - 1, MASK>(nt_used, a, lds, b, br, t_off, g, s, dl, ctx, pg_begin, pg_end);
             return;
         }
     }
-    partition_body<D, G, NTU, MASK>(a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+    partition_body<D, G, NTU, MASK>(a, lds, b, br, t_off, g, s, dl, ctx, pg_begin, pg_end);
 }
 
 template <int D, int G, int MASK>
@@ -853,9 +871,9 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int g = bg % a.Hkv;
     const int b = bg / a.Hkv;
 
-    const int dl = a.draft_lens[b];
-    const int ctx = a.context_lens[b];                        // both loads in flight together
-    if (dl <= 0) return;                                      // request is a no-op
+    const BlockReq rq = block_req(a.draft_lens, a.context_lens, b, a.blocks_per_req);
+    const int dl = rq.dl, ctx = rq.ctx;
+    if (dl <= 0) return;                                      // request (or block) is a no-op
     const int n_pages = (ctx + kPage - 1) / kPage;
     // a window hides every key before the first one the block's first draft sees
     const int lo_page = MASK == kMaskWindow ? max(0, ctx - dl + 1 - a.window) / kPage : 0;
@@ -868,7 +886,7 @@ void verify_partition_kernel(const VerifyArgs a) {
         }
         return;
     }
-    dispatch_tiles<D, G, G, MASK>((rows + 15) >> 4, a, lds, b, g, s, dl, ctx, pg_begin, pg_end);
+    dispatch_tiles<D, G, G, MASK>((rows + 15) >> 4, a, lds, b, rq.req, rq.t_off, g, s, dl, ctx, pg_begin, pg_end);
 }
 
 // ---------------------------------------------------------------------------
@@ -922,7 +940,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
     const int v = (blockIdx.x / 4) % NSL;
     const int r = blockIdx.x / (4 * NSL);
     const int g = blockIdx.y, b = blockIdx.z;
-    const int lim = G * a.draft_lens[b];
+    const BlockReq rq = block_req(a.draft_lens, nullptr, b, a.blocks_per_req);
+    const int lim = G * rq.dl;
     if (32 * r >= lim) return;                                // uniform: no row of this tile is a draft row
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int row = 32 * r + (lane & 31);
@@ -984,7 +1003,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
     u32x2_t o;
     o[0] = (uint32_t)f32_to_bf16_rne(st.acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(st.acc[1] * inv) << 16);
     o[1] = (uint32_t)f32_to_bf16_rne(st.acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(st.acc[3] * inv) << 16);
-    *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.T_max + t) * a.Hq + hq) * D + d) = o;
+    *reinterpret_cast<u32x2_t*>(a.out + (((size_t)rq.req * a.T_max + rq.t_off + t) * a.Hq + hq) * D + d) = o;
 }
 
 // ---------------------------------------------------------------------------

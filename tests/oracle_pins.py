@@ -359,6 +359,16 @@ def pin_attn_dense_quantized(orc, seed=23):
         assert rel_err(out[b, :d], ref) <= 1e-12
 
 
+def pin_prefill_long_blocks_dense(orc, seed=37):
+    """Chunked prefill is the same definition with a block of any length: chunks
+    of 80 and 37 tokens after a prior context, and chunks that are the whole
+    context (no prior keys), against the dense brute force."""
+    _check_dense(orc, _small_direct(seed, context_lens=[150, 60], draft_lens=[80, 37], T_max=80,
+                                    num_pages=24), 1e-12)
+    _check_dense(orc, _small_direct(seed + 1, context_lens=[33, 70], draft_lens=[33, 70], T_max=70,
+                                    Hq=8, Hkv=2, D=32, num_pages=16), 1e-12)
+
+
 def pin_attn_prefix_consistency(orc, seed=24):
     """Row t of a block equals a one-token call at context pos_t + 1 (T=1 is
     ordinary decode; losslessness against autoregressive decoding)."""
@@ -681,6 +691,7 @@ ALL_PINS = [
     pin_attn_dense_random,
     pin_attn_dense_quantized,
     pin_attn_prefix_consistency,
+    pin_prefill_long_blocks_dense,
     pin_attn_shared_prefix_equals_private,
     pin_attn_page_permutation,
     pin_attn_closed_forms,
