@@ -56,7 +56,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0                            # dense fp16/bf16 MFMA, MI355X
 METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak) at 32K ctx, T=16"
 WORKLOAD = "verify 1 req x ctx 32768, T=16 drafts, 24q/4kv heads, D=256, int8 KV in 16-token pages"
-PART_KERNEL = "verify_partition_kernel"
+PART_KERNEL = "verify_partition_kernel<256, 6, 0>"        # the causal instantiation at D = 256, G = 6
 TRAFFIC_SUMMARY = ROOT / "profiles" / "verify_partition_d256_ctx32k_hbm_traffic.md"
 # sources the partition kernel is compiled from (their hash stamps counter summaries)
 KERNEL_SOURCES = ["speculative_decode_attention_amd/csrc/verify_attn.hip",
@@ -327,7 +327,7 @@ def main():
                    "partition_us_mall_warm": round(part_us_warm, 3),
                    "hbm_read_ceiling_pages_gbs": round(stream_gbs, 1),
                    "verify_pct_of_hbm_peak": round(100 * part_bytes / (us_verify * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)},
-        "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel<256,6>",
+        "roofline": {"bound": "hbm", "kernel": PART_KERNEL,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": trec["hbm_bytes_per_launch"] if trec else None,
@@ -571,7 +571,7 @@ def oracle_one_thread_child(d):
 # ---------------------------------------------------------------------------
 
 def _short(name: str) -> str:
-    name = name.replace("void ", "")
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
     if "splash::" in name:
         return name.split("(")[0].replace("splash::", "")
     return name[:60]
@@ -654,7 +654,7 @@ def summarize_traffic(fetch_dir, write_dir, cmd):
         fk, wk = float(np.mean(fetch[k])), float(np.mean(write.get(k, [0.0])))
         fb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
         print(f"| `{_short(k)}` | {len(fetch[k])} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
-        if PART_KERNEL in k and "256" in _short(k):
+        if PART_KERNEL in k:
             rec = {"kernel": _short(k), "source_hash": kernel_source_hash(),
                    "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                    "hbm_bytes_per_launch": round(fb + wb), "fetch_factor": round(f_fac, 4),

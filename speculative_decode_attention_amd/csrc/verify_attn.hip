@@ -62,8 +62,9 @@ constexpr int kKAhead = 3;     // K(i + 3) is issued at step i
 constexpr int kIdAhead = 7;    // the page id of step i + 7 is copied at step i
 constexpr int kIdRing = 8;
 // how a draft sees the block and the context: the causal chain, a tree of
-// candidates (per-draft bit masks), or a sliding window over the keys
-constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2;
+// candidates (per-draft bit masks), a sliding window over the keys, or the
+// causal chain of a prefill chunk cut into several 16-token blocks per request
+constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2, kMaskChunked = 3;
 
 // A work item's request.  Verify: request b itself.  A prefill chunk of
 // n_b tokens is cut into blocks of 16 (blocks_per_req of them per request):
@@ -871,7 +872,7 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int g = bg % a.Hkv;
     const int b = bg / a.Hkv;
 
-    const BlockReq rq = block_req(a.draft_lens, a.context_lens, b, a.blocks_per_req);
+    const BlockReq rq = block_req(a.draft_lens, a.context_lens, b, MASK == kMaskChunked ? a.blocks_per_req : 1);
     const int dl = rq.dl, ctx = rq.ctx;
     if (dl <= 0) return;                                      // request (or block) is a no-op
     const int n_pages = (ctx + kPage - 1) / kPage;
@@ -931,7 +932,7 @@ __device__ __forceinline__ void merge_rescale(MergeState& st, float mn) {
     st.M = mn;
 }
 
-template <int D, int G>
+template <int D, int G, bool CHUNKED>
 __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
     constexpr int NSL = Cfg<D, G>::NSL, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
     __shared__ float xch[kMergeWaves - 1][6][64];
@@ -940,7 +941,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
     const int v = (blockIdx.x / 4) % NSL;
     const int r = blockIdx.x / (4 * NSL);
     const int g = blockIdx.y, b = blockIdx.z;
-    const BlockReq rq = block_req(a.draft_lens, nullptr, b, a.blocks_per_req);
+    const BlockReq rq = block_req(a.draft_lens, nullptr, b, CHUNKED ? a.blocks_per_req : 1);
     const int lim = G * rq.dl;
     if (32 * r >= lim) return;                                // uniform: no row of this tile is a draft row
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1016,7 +1017,9 @@ static hipError_t launch_partition_dg(const VerifyArgs& a, hipStream_t stream) {
     const long blocks = (long)a.B * a.Hkv * a.num_splits;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (a.block_masks != nullptr)
+    if (a.blocks_per_req > 1)
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskChunked>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+    else if (a.block_masks != nullptr)
         hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskTree>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     else if (a.window > 0)
         hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskWindow>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
@@ -1038,7 +1041,10 @@ static hipError_t launch_merge_tiled_dg(const TiledMergeArgs& a, hipStream_t str
     if (a.B <= 0 || a.Hkv <= 0) return hipSuccess;
     if (a.B > 65535 || a.Hkv > 65535) return hipErrorInvalidConfiguration;
     const dim3 grid(Cfg<D, G>::NT32 * Cfg<D, G>::NSL * 4, (unsigned)a.Hkv, (unsigned)a.B);
-    hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G>), grid, dim3(kMergeWaves * 64), 0, stream, a);
+    if (a.blocks_per_req > 1)
+        hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, true>), grid, dim3(kMergeWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, false>), grid, dim3(kMergeWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
