@@ -63,6 +63,7 @@ KERNEL_SOURCES = ["speculative_decode_attention_amd/csrc/verify_attn.hip",
                   "speculative_decode_attention_amd/csrc/device.h",
                   "speculative_decode_attention_amd/csrc/launch.h"]
 CALIB_MIB = 512
+PMC_STEPS = 20                                            # --steps of the counter runs
 DEFAULT_STEPS = 200
 
 
@@ -287,6 +288,7 @@ def main():
     stream_gbs = read_ceiling_gbs(dev)
     accept = accept_leg(dev, args.steps)
     prefill = prefill_leg(dev, args.steps)
+    shared = shared_prefix_leg(dev, args.steps)
     part_bytes = verify_bytes(ctx, Hkv, D, T, Hq)
     achieved = part_bytes / (part_us * 1e-6) / 1e9
 
@@ -338,6 +340,7 @@ def main():
         "cpu_baseline": cpu,
         "accept": accept,
         "prefill": prefill,
+        "shared_prefix": shared,
     }
     print(json.dumps(line), flush=True)
 
@@ -439,6 +442,68 @@ def prefill_leg(dev, steps: int) -> dict:
             "frac_of_fp16_mfma_peak": round(flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "distinct_bytes": kv_bytes, "distinct_gbs": round(kv_bytes / (us * 1e-6) / 1e9, 1),
             "tokens_per_s": round(chunk / (us * 1e-6), 0)}
+
+
+def shared_leg_launches(steps: int) -> int:
+    """Partition launches the shared-prefix leg makes (it runs last): warm-up + timed."""
+    return 5 + max(steps // 2, 10)
+
+
+def shared_prefix_leg(dev, steps: int) -> dict:
+    """Four concurrent requests sharing one 24,576-token prefix through identical
+    block-table entries, plus 2,048 private tokens each (T = 16, 24 q / 4 kv
+    heads, D = 256).  Bounds: HBM over the distinct bytes (shared pages once)
+    and the fp16 MFMA peak over the FLOPs (4 * D per valid row and visible key)."""
+    import torch
+    import speculative_decode_attention_amd as sda
+    from speculative_decode_attention_amd import synth
+    wl = synth.make_config(4)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    pools = [up(a) for a in (wl.k_pool, wl.v_pool, wl.k_scale, wl.v_scale)]
+    for ph in wl.appends:
+        sda.splash_kv_append_int8(up(ph.k_src), up(ph.v_src), *pools, up(ph.block_table),
+                                  up(ph.context_lens), up(ph.draft_lens))
+    q, bt, cl, dl = up(wl.q), up(wl.block_table), up(wl.context_lens), up(wl.draft_lens)
+    out = torch.empty_like(q)
+    ctx = int(wl.max_context_len)
+    S = sda.splash_verify_attn_default_splits(wl.B, wl.Hkv, ctx, wl.P, wl.D)
+    ws = torch.empty(max(sda.splash_verify_attn_workspace_bytes(wl.B, wl.T_max, wl.Hq, wl.D, S), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        sda.splash_verify_attn(q, out, *pools, bt, cl, dl, ctx, wl.sm_scale, workspace=ws)
+
+    n = shared_leg_launches(steps) - 5
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(n * 40e-6 * 2.0e9))
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    d = [int(x) for x in wl.draft_lens]
+    ctxs = [int(x) for x in wl.context_lens]
+    distinct_tokens = len(np.unique(wl.block_table[:, :-(-ctx // wl.P)])) * wl.P
+    nbytes = (distinct_tokens * wl.Hkv * (2 * wl.D + 4) + sum(d) * wl.Hq * wl.D * 4
+              + wl.block_table[:, :-(-ctx // wl.P)].size * 4 + 8 * wl.B)
+    flops = sum(4 * wl.D * wl.Hq * sum(c - dd + t + 1 for t in range(dd)) for c, dd in zip(ctxs, d))
+    hbm_us = nbytes / (HBM_PEAK_GBS * 1e3)
+    mfma_us = flops / (MFMA_F16_PEAK_TFLOPS * 1e6)
+    del pools, q, out, ws
+    return {"workload": "4 requests sharing a 24576-token prefix + 2048 private tokens each, T=16",
+            "us_per_call": round(us, 2), "splits": S, "distinct_bytes": nbytes, "flops": flops,
+            "hbm_bound_us": round(hbm_us, 2), "mfma_bound_us": round(mfma_us, 2),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "frac_of_fp16_mfma_peak": round(mfma_us / us, 4),
+            "distinct_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def read_ceiling_gbs(dev) -> float:
@@ -602,6 +667,8 @@ def summarize_stats(d, cmd):
     us = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                    for r in trace if PART_KERNEL in r["Kernel_Name"]])
     n = DEFAULT_STEPS
+    n_shared = shared_leg_launches(n)
+    us, us_shared = us[:-n_shared], us[-n_shared:]
     if len(us) > 3 * n:
         print("\nPartition launches by phase of the run (kernel trace):\n")
         print("| phase | launches | mean µs |")
@@ -609,13 +676,17 @@ def summarize_stats(d, cmd):
         for name, seg in (("verify graphs (with the merge)", us[:-3 * n]),
                           ("back to back, 16 rotating cache replicas (`roofline.mean_launch_us`)", us[-3 * n:-2 * n]),
                           ("one event pair per launch", us[-2 * n:-n]),
-                          ("back to back, one replica (MALL-warm)", us[-n:])):
+                          ("back to back, one replica (MALL-warm)", us[-n:]),
+                          ("shared-prefix leg: 4 requests, 24,576 shared + 2,048 private tokens each",
+                           us_shared)):
             print(f"| {name} | {len(seg)} | {seg.mean():.2f} |")
 
 
 def _per_dispatch(d, counter):
+    """Counter value per dispatch, per kernel name, in dispatch order."""
     per = {}
-    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+    rows = sorted(csv.DictReader(open(_find(d, "counter_collection.csv"))), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
         if r["Counter_Name"] != counter:
             continue
         per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
@@ -636,6 +707,14 @@ def summarize_traffic(fetch_dir, write_dir, cmd):
         return calib_bytes / (float(np.median(vals)) * 1024.0)
 
     f_fac, w_fac = calib(fetch), calib(write)
+    # the shared-prefix leg runs last: its partition launches are reported on their own
+    n_shared = shared_leg_launches(PMC_STEPS)
+    shared = {}
+    for per, key in ((fetch, "f"), (write, "w")):
+        for k in list(per):
+            if PART_KERNEL in k:
+                shared[key] = per[k][-n_shared:]
+                per[k] = per[k][:-n_shared]
     part = [k for k in fetch if PART_KERNEL in k]
     if not part:
         raise SystemExit("no partition kernel in the counter output")
@@ -659,6 +738,11 @@ def summarize_traffic(fetch_dir, write_dir, cmd):
                    "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                    "hbm_bytes_per_launch": round(fb + wb), "fetch_factor": round(f_fac, 4),
                    "write_factor": round(w_fac, 4)}
+    if shared:
+        fb, wb = float(np.mean(shared["f"])) * 1024 * f_fac, float(np.mean(shared["w"])) * 1024 * w_fac
+        print(f"| `{_short(PART_KERNEL)}`, shared-prefix leg (4 requests, 24,576 shared + 2,048 private "
+              f"tokens each) | {len(shared['f'])} | {np.mean(shared['f']):.0f} | {np.mean(shared['w']):.0f} | "
+              f"{fb / 1e6:.2f} | {wb / 1e6:.2f} |")
     print("\nRecord read by bench.py (`roofline.traffic`, only while the source hash matches):\n")
     print(json.dumps(rec))
 
