@@ -1,12 +1,9 @@
 // kv_append.hip -- the write side of the int8 paged KV cache (gfx950).
 //
-// The pages say the decode kernel reads an 8-bit KV cache (Splash community
-// summary on discuss.pytorch.kr, section "Metal kernels generated to shape")
-// and that KV precision is a setting (localai.co.kr guide to Splash 1.3.0); they
-// do not describe the quantiser.  This kernel implements the library's
-// documented one: symmetric int8 with one fp16 scale per (token, kv head),
-// scale = binary16(amax / 127), codes = clamp(rint(x / scale), -127, 127), all in
-// IEEE fp32 so that it is bit-exact and reproducible.
+// The quantiser (quant.h) is symmetric int8 with one fp16 scale per (token, kv
+// head), in IEEE fp32 so that it is bit-exact and reproducible; the pages fix
+// only that the cache is 8-bit (Splash community summary on discuss.pytorch.kr,
+// section "Metal kernels generated to shape").
 //
 // One wave per (request, token, kv head) row.  Each lane holds D/64 values; the
 // row maximum is a wave reduction.  K rows are stored as D contiguous bytes
@@ -15,54 +12,9 @@
 // few hundred bytes per row and is launch-latency bound for a draft block.
 #include "device.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace splash {
-
-template <int D, bool SRC_BF16>
-__device__ __forceinline__ void load_row(const void* src, size_t off, float (&x)[D / 64]) {
-    constexpr int E = D / 64;
-    if constexpr (SRC_BF16) {
-        const uint16_t* p = static_cast<const uint16_t*>(src) + off;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = bit_cast<float>((uint32_t)p[e] << 16);
-    } else {
-        const float* p = static_cast<const float*>(src) + off;
-        if constexpr (E == 4) {
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
-            x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = p[e];
-        }
-    }
-}
-
-// Quantise one row held across the wave; returns this lane's codes packed
-// little-endian (code e in byte e) and the binary16 scale bits.
-template <int D>
-__device__ __forceinline__ uint32_t quantize_row(const float (&x)[D / 64], uint16_t& s16_bits) {
-    constexpr int E = D / 64;
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = wave_max(amax);
-    const float s32 = amax / 127.0f;                 // IEEE fp32 division
-    const _Float16 s16 = (_Float16)s32;              // round to nearest even
-    const float s = (float)s16;                      // exact widening
-    s16_bits = bit_cast<uint16_t>(s16);
-    uint32_t packed = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        int c = 0;
-        if (s != 0.0f) {
-            float r = __builtin_rintf(x[e] / s);     // IEEE division, ties to even
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            c = (int)r;
-        }
-        packed |= ((uint32_t)(c & 0xff)) << (8 * e);
-    }
-    return packed;
-}
 
 template <int D, bool SRC_BF16>
 __global__ __launch_bounds__(256) void kv_append_int8_kernel(
@@ -72,7 +24,6 @@ __global__ __launch_bounds__(256) void kv_append_int8_kernel(
     const int32_t* __restrict__ block_table, int max_pages_per_seq,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ draft_lens,
     int B, int T_max, int Hkv) {
-    constexpr int E = D / 64;
     const int lane = threadIdx.x & 63;
     const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);   // one wave per row
     if (item >= (long)B * T_max * Hkv) return;
@@ -84,29 +35,8 @@ __global__ __launch_bounds__(256) void kv_append_int8_kernel(
     if (t >= dl) return;                              // whole wave leaves together
     const int pos = context_lens[b] - dl + t;
     const int page = block_table[(size_t)b * max_pages_per_seq + pos / kPage];
-    const int slot = pos % kPage;
-    const size_t src = ((size_t)bt * Hkv + g) * D + (size_t)lane * E;
-    const size_t pg = (size_t)page * Hkv + g;
-
-    float x[E];
-    uint16_t s16;
-
-    // K: the lane's E codes are contiguous in the token row
-    load_row<D, SRC_BF16>(k_new, src, x);
-    uint32_t codes = quantize_row<D>(x, s16);
-    int8_t* kdst = k_pool + (pg * kPage + slot) * D + (size_t)lane * E;
-    if constexpr (E == 4) *reinterpret_cast<uint32_t*>(kdst) = codes;
-    else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)codes;
-    else *kdst = (int8_t)codes;
-    if (lane == 0) k_scale[pg * kPage + slot] = s16;
-
-    // V: a page is two d-major tiles of 8 tokens, [P/8][D][8]; one byte per d
-    load_row<D, SRC_BF16>(v_new, src, x);
-    codes = quantize_row<D>(x, s16);
-    int8_t* vdst = v_pool + ((pg * (kPage / 8) + slot / 8) * D + (size_t)lane * E) * 8 + slot % 8;
-#pragma unroll
-    for (int e = 0; e < E; ++e) vdst[e * 8] = (int8_t)((codes >> (8 * e)) & 0xff);
-    if (lane == 0) v_scale[pg * kPage + slot] = s16;
+    append_token_row<D, SRC_BF16>(k_new, v_new, ((size_t)bt * Hkv + g) * D, k_pool, v_pool, k_scale, v_scale,
+                                  (size_t)page * Hkv + g, pos % kPage, lane);
 }
 
 template <int D>

@@ -74,11 +74,13 @@ constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2, kMaskChunked = 3;
 struct BlockReq {
     int req, t_off, dl, ctx;
 };
+// A draft length past T_max breaks the caller's contract; it is cut to T_max so
+// that no q or out row outside the request is touched.
 __device__ __forceinline__ BlockReq block_req(const int32_t* draft_lens, const int32_t* context_lens, int b,
-                                              int nblk) {
+                                              int nblk, int T_max) {
     const int br = nblk == 1 ? b : b / nblk;
     const int t_off = 16 * (b - br * nblk);
-    const int d_all = draft_lens[br];
+    const int d_all = min(draft_lens[br], T_max);
     const int ctx_all = context_lens != nullptr ? context_lens[br] : 0;
     const int dl = nblk == 1 ? d_all : min(max(d_all - t_off, 0), 16);
     return BlockReq{br, t_off, dl, ctx_all - (d_all - t_off - dl)};
@@ -872,7 +874,8 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int g = bg % a.Hkv;
     const int b = bg / a.Hkv;
 
-    const BlockReq rq = block_req(a.draft_lens, a.context_lens, b, MASK == kMaskChunked ? a.blocks_per_req : 1);
+    const BlockReq rq = block_req(a.draft_lens, a.context_lens, b, MASK == kMaskChunked ? a.blocks_per_req : 1,
+                                  a.T_max);
     const int dl = rq.dl, ctx = rq.ctx;
     if (dl <= 0) return;                                      // request (or block) is a no-op
     const int n_pages = (ctx + kPage - 1) / kPage;
@@ -941,7 +944,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
     const int v = (blockIdx.x / 4) % NSL;
     const int r = blockIdx.x / (4 * NSL);
     const int g = blockIdx.y, b = blockIdx.z;
-    const BlockReq rq = block_req(a.draft_lens, nullptr, b, CHUNKED ? a.blocks_per_req : 1);
+    const BlockReq rq = block_req(a.draft_lens, nullptr, b, CHUNKED ? a.blocks_per_req : 1, a.T_max);
     const int lim = G * rq.dl;
     if (32 * r >= lim) return;                                // uniform: no row of this tile is a draft row
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;

@@ -168,3 +168,22 @@ def test_append_quantiser_edge_rows_bit_exact():
     for h, d in zip(host, dev):
         got = d.cpu().numpy()
         assert np.array_equal(got.view(h.dtype) if h.dtype == np.uint16 else got, h)
+
+
+@pytest.mark.parametrize("S", [1, 5])
+def test_draft_length_past_t_max_is_cut_to_t_max(S):
+    """A draft length above T_max breaks the caller's contract; the kernels cut it
+    to T_max, so the call gives the bits of the call with draft_lens = T_max and
+    writes no row outside its requests (a guard request after out stays NaN)."""
+    prep = small(2, T_max=12, draft_lens=[12, 7, 12])
+    wl = prep.wl
+    ref = prep.run(num_splits=S).cpu().numpy()
+    bad = wl.draft_lens.copy()
+    bad[0], bad[2] = 15, 16
+    big = torch.full((wl.B + 1, wl.T_max, wl.Hq, wl.D), BF16_NAN, dtype=torch.int16, device="cuda")
+    sda.splash_verify_attn(prep.q, big[:wl.B], *prep.g_pools, prep.bt, prep.ctx, up(bad), wl.max_context_len,
+                           wl.sm_scale, num_splits=S)
+    torch.cuda.synchronize()
+    got = big.cpu().numpy()
+    assert np.array_equal(got[:wl.B], ref)
+    assert np.all(got[wl.B].view(np.uint16) == BF16_NAN)
