@@ -288,6 +288,7 @@ def main():
     stream_gbs = read_ceiling_gbs(dev)
     accept = accept_leg(dev, args.steps)
     prefill = prefill_leg(dev, args.steps)
+    scaling = context_scaling_leg(dev, args.steps)
     shared = shared_prefix_leg(dev, args.steps)
     part_bytes = verify_bytes(ctx, Hkv, D, T, Hq)
     achieved = part_bytes / (part_us * 1e-6) / 1e9
@@ -341,6 +342,7 @@ def main():
         "accept": accept,
         "prefill": prefill,
         "shared_prefix": shared,
+        "context_scaling": scaling,
     }
     print(json.dumps(line), flush=True)
 
@@ -442,6 +444,93 @@ def prefill_leg(dev, steps: int) -> dict:
             "frac_of_fp16_mfma_peak": round(flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "distinct_bytes": kv_bytes, "distinct_gbs": round(kv_bytes / (us * 1e-6) / 1e9, 1),
             "tokens_per_s": round(chunk / (us * 1e-6), 0)}
+
+
+SCALING_CONTEXTS = (8192, 32768, 131072)
+
+
+def scaling_replicas(ctx: int) -> int:
+    """Page replicas the context-scaling leg rotates over at this context."""
+    num_pages = ctx // 16 + 8
+    pool_bytes = num_pages * 4 * 16 * (2 * 256 + 2 * 2)
+    return max(2, -(-(512 << 20) // pool_bytes))
+
+
+def scaling_leg_launches(steps: int) -> int:
+    """Partition launches the context-scaling leg makes (eager warm-up, one warm
+    replay of every graph, the timed replays; all contexts)."""
+    return sum(R + R + max(1, max(steps // 2, 2 * R) // R) * R for R in map(scaling_replicas, SCALING_CONTEXTS))
+
+
+def context_scaling_leg(dev, steps: int) -> dict:
+    """The verify call (one request, T = 16, 24 q / 4 kv heads, D = 256) at 8K,
+    32K and 128K tokens of context.  The per-launch costs (launch, start-up,
+    pipeline fill and drain, partial stores, merge) are fixed, so the rate
+    rises with the context.  Each context's pages are repeated until the calls
+    rotate over more than 512 MB (twice the Infinity Cache), so the pages come
+    from HBM.  The cache holds the library's quantisation of Gaussian rows, as
+    in the 32K workload above (the value distribution matters: widely spread
+    scores move the softmax reference more often)."""
+    import torch
+    import speculative_decode_attention_amd as sda
+    from speculative_decode_attention_amd import synth
+    res = {}
+    for ctx in SCALING_CONTEXTS:
+        wl = synth.make_workload("scaling", 61, B=1, context_lens=[ctx], T_max=16, Hq=24, Hkv=4, D=256,
+                                 num_pages=ctx // 16 + 8)
+        host = (wl.k_pool, wl.v_pool, wl.k_scale.view(np.int16), wl.v_scale.view(np.int16))
+        one = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in host]
+        for ph in wl.appends:
+            sda.splash_kv_append_int8(torch.from_numpy(ph.k_src).to(dev), torch.from_numpy(ph.v_src).to(dev), *one,
+                                      torch.from_numpy(ph.block_table).to(dev), torch.from_numpy(ph.context_lens).to(dev),
+                                      torch.from_numpy(ph.draft_lens).to(dev))
+        wl.appends = None                                     # the source rows are no longer needed
+        R = scaling_replicas(ctx)
+        assert R * sum(a.nbytes for a in host) >= 512 << 20
+        pools = [a.repeat((R,) + (1,) * (a.dim() - 1)) for a in one]
+        del one
+        bts = [torch.from_numpy(wl.block_table + r * wl.num_pages).to(dev) for r in range(R)]
+        q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
+        cl, dl = torch.from_numpy(wl.context_lens).to(dev), torch.from_numpy(wl.draft_lens).to(dev)
+        out = torch.empty_like(q)
+        S = sda.splash_verify_attn_default_splits(1, 4, ctx, 16, 256)
+        ws = torch.empty(max(sda.splash_verify_attn_workspace_bytes(1, 16, 24, 256, S), 16), dtype=torch.uint8,
+                         device=dev)
+
+        def call(r):
+            sda.splash_verify_attn(q, out, *pools, bts[r], cl, dl, ctx, wl.sm_scale, workspace=ws)
+
+        for r in range(R):
+            call(r)
+        torch.cuda.synchronize()
+        # graphs of C consecutive calls on different replicas (host launch rate does not show)
+        C = min(R, 16)
+        graphs = []
+        for g0 in range(0, R, C):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                for r in range(g0, min(g0 + C, R)):
+                    call(r)
+            graphs.append(g)
+        reps = max(1, max(steps // 2, 2 * R) // R)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(reps * len(graphs) * 20e-6 * 2.0e9))
+        e0.record()
+        for _ in range(reps):
+            for g in graphs:
+                g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (reps * R) * 1e3
+        nbytes = verify_bytes(ctx, 4, 256, 16, 24)
+        res[f"ctx_{ctx}"] = {"us_per_call": round(us, 2), "bytes": nbytes, "splits": S,
+                             "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                             "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del graphs, pools, bts, q, out, ws
+    return res
 
 
 def shared_leg_launches(steps: int) -> int:
@@ -667,8 +756,9 @@ def summarize_stats(d, cmd):
     us = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                    for r in trace if PART_KERNEL in r["Kernel_Name"]])
     n = DEFAULT_STEPS
-    n_shared = shared_leg_launches(n)
+    n_shared, n_scaling = shared_leg_launches(n), scaling_leg_launches(n)
     us, us_shared = us[:-n_shared], us[-n_shared:]
+    us = us[:-n_scaling]                                  # the context-scaling leg (other contexts)
     if len(us) > 3 * n:
         print("\nPartition launches by phase of the run (kernel trace):\n")
         print("| phase | launches | mean µs |")
@@ -708,13 +798,13 @@ def summarize_traffic(fetch_dir, write_dir, cmd):
 
     f_fac, w_fac = calib(fetch), calib(write)
     # the shared-prefix leg runs last: its partition launches are reported on their own
-    n_shared = shared_leg_launches(PMC_STEPS)
+    n_shared, n_scaling = shared_leg_launches(PMC_STEPS), scaling_leg_launches(PMC_STEPS)
     shared = {}
     for per, key in ((fetch, "f"), (write, "w")):
         for k in list(per):
             if PART_KERNEL in k:
                 shared[key] = per[k][-n_shared:]
-                per[k] = per[k][:-n_shared]
+                per[k] = per[k][:-(n_shared + n_scaling)]     # the context-scaling leg's are other contexts
     part = [k for k in fetch if PART_KERNEL in k]
     if not part:
         raise SystemExit("no partition kernel in the counter output")
