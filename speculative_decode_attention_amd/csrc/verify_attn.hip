@@ -49,6 +49,12 @@
 //    set.
 //  * The epilogue divides by the row sums and writes bf16 rows (one split) or
 //    fp16 partial tiles with their natural-log log-sum-exp (several splits).
+//  * Visibility is a compile-time mode of the kernel, so each variant keeps
+//    its own straight-line step: the causal chain; a tree of candidates (bit
+//    masks per draft, staged in LDS); a sliding window of the last W keys
+//    (splits start at the first visible page); and the causal chain of a
+//    prefill chunk cut into 16-token blocks, each a verify block over the cache
+//    up to its own last token.
 #include <math.h>
 
 #include "device.h"
