@@ -759,6 +759,9 @@ def summarize_stats(d, cmd):
     n_shared, n_scaling = shared_leg_launches(n), scaling_leg_launches(n)
     us, us_shared = us[:-n_shared], us[-n_shared:]
     us = us[:-n_scaling]                                  # the context-scaling leg (other contexts)
+    print(f"\nThe table's `{_short(PART_KERNEL)}` row also holds the launches of the shared-prefix and "
+          f"context-scaling legs (other workloads); over the {len(us)} launches of the 32K workload alone "
+          f"the mean is {us.mean():.2f} µs.")
     if len(us) > 3 * n:
         print("\nPartition launches by phase of the run (kernel trace):\n")
         print("| phase | launches | mean µs |")
