@@ -19,6 +19,11 @@ BF16_NAN = 0x7FC0
 # |o| >= 2.56)
 REL_L2 = 2e-3
 ABS = 1e-2
+# per element, beside the above: |got - ref| <= half an ulp of bf16(ref) + MAG_REL * mag, where
+# mag = sum_j w_j |v_j| / sum_j w_j is the attention of |V| (the size of the row before the
+# signs of V cancel).  The kernel rounds p, P' = p s_v and split partials to fp16, each a
+# relative 2^-11 of that size; 2^-8 leaves a margin of 2 over their sum.
+MAG_REL = 2.0 ** -8
 
 
 def log(msg):
@@ -68,13 +73,19 @@ def _round_bf16(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
 
 
-def assert_attn_ok(got, ref, where):
+def assert_attn_ok(got, ref, where, mag=None):
+    """mag: the attention of |V| for the same rows (enables the per-element bound)."""
     e = attn_error(got, ref)
     log(f"  {where}: rel_l2={e['rel_l2']:.3e} max|err|={e['max_abs']:.3e} "
         f"bound_excess={e['bound_excess']:.2e} ulps_vs_bf16(ref)={e['max_ulps_vs_bf16_ref']:.2f}")
     assert e["finite"], f"{where}: non-finite output"
     assert e["rel_l2"] <= REL_L2, f"{where}: relative L2 {e['rel_l2']:.3e}"
     assert e["bound_excess"] <= 0, f"{where}: an element exceeds 1e-2 + half a bf16 ulp"
+    if mag is not None:
+        ratio = (np.abs(got - ref) - half_ulp_bf16(ref)) / np.maximum(mag, 1e-300)
+        worst = float(ratio.max()) if ratio.size else 0.0
+        log(f"    per element: max (|err| - half ulp) / mag = {worst:.2e} (bound {MAG_REL:.2e})")
+        assert worst <= MAG_REL, f"{where}: an element exceeds half a bf16 ulp + {MAG_REL:.2e} * mag"
     return e
 
 
@@ -146,6 +157,7 @@ class Prepared:
             sda.splash_kv_append_int8(up(ph.k_src), up(ph.v_src), *self.g_pools, up(ph.block_table),
                                       up(ph.context_lens), up(ph.draft_lens))
         torch_mod().cuda.synchronize()
+        self._abs_pools = None
         self.q = up(wl.q)
         self.bt = up(wl.block_table)
         self.ctx = up(wl.context_lens)
@@ -177,10 +189,19 @@ class Prepared:
         return np.array([(b, t, h) for b in range(wl.B) for t in range(int(wl.draft_lens[b]))
                          for h in range(wl.Hq)], dtype=np.int32)
 
-    def oracle_rows(self, rows):
+    @property
+    def abs_pools(self):
+        """The oracle's pools with every V code replaced by its absolute value (codes are
+        never -128): the attention over them is sum_j w_j |v_j| / sum_j w_j."""
+        if self._abs_pools is None:
+            kp, vp, ks, vs = self.pools
+            self._abs_pools = [kp, np.abs(vp.astype(np.int16)).astype(np.int8), ks, vs]
+        return self._abs_pools
+
+    def oracle_rows(self, rows, abs_v=False):
         wl = self.wl
-        return oracle.load().verify_attn_rows(wl.q, *self.pools, wl.block_table, wl.context_lens,
-                                              wl.draft_lens, wl.Hkv, wl.sm_scale, rows)
+        return oracle.load().verify_attn_rows(wl.q, *(self.abs_pools if abs_v else self.pools), wl.block_table,
+                                              wl.context_lens, wl.draft_lens, wl.Hkv, wl.sm_scale, rows)
 
 
 _cache = {}

@@ -22,7 +22,7 @@ def check(prep, S, where, sample=None):
         rng = np.random.default_rng(len(rows))
         rows = rows[np.sort(rng.choice(len(rows), sample, replace=False))]
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, prep.oracle_rows(rows), where)
+    assert_attn_ok(got, prep.oracle_rows(rows), where, mag=prep.oracle_rows(rows, abs_v=True))
     for b in range(wl.B):
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN), f"{where}: row written"
 

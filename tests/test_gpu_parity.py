@@ -45,7 +45,7 @@ def test_verify_matches_oracle(cfg):
         rows = rows[np.sort(rng.choice(len(rows), SAMPLE[cfg], replace=False))]
     ref = prep.oracle_rows(rows)
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, ref, f"config {cfg} ({len(rows)} rows)")
+    assert_attn_ok(got, ref, f"config {cfg} ({len(rows)} rows)", mag=prep.oracle_rows(rows, abs_v=True))
     # rows past each request's draft are never written
     for b in range(wl.B):
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
@@ -58,7 +58,7 @@ def test_split_count_sweep(S):
     rows = prep.valid_rows()
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
     ref = prep.oracle_rows(rows)
-    assert_attn_ok(got, ref, f"config 2, {S} splits")
+    assert_attn_ok(got, ref, f"config 2, {S} splits", mag=prep.oracle_rows(rows, abs_v=True))
 
 
 @pytest.mark.parametrize("v_mag", [1.0, 3e4])

@@ -35,7 +35,7 @@ def check_prefill(prep, num_splits, where, sample=None):
         rows = rows[np.sort(rng.choice(len(rows), sample, replace=False))]
     ref = prep.oracle_rows(rows)
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, ref, where)
+    assert_attn_ok(got, ref, where, mag=prep.oracle_rows(rows, abs_v=True))
     for b in range(wl.B):                                     # rows past each chunk stay untouched
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
 

@@ -34,7 +34,9 @@ def check_tree(prep, masks, num_splits, where):
                                            wl.Hkv, wl.sm_scale, masks)
     rows = prep.valid_rows()
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, ref[rows[:, 0], rows[:, 1], rows[:, 2]], where)
+    mag = oracle.load().verify_attn_masked(wl.q, *prep.abs_pools, wl.block_table, wl.context_lens, wl.draft_lens,
+                                           wl.Hkv, wl.sm_scale, masks)
+    assert_attn_ok(got, ref[rows[:, 0], rows[:, 1], rows[:, 2]], where, mag=mag[rows[:, 0], rows[:, 1], rows[:, 2]])
     for b in range(wl.B):                                     # rows past the draft stay untouched
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
 
