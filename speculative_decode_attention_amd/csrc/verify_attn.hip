@@ -941,23 +941,28 @@ __device__ __forceinline__ void merge_rescale(MergeState& st, float mn) {
     st.M = mn;
 }
 
-template <int D, int G, bool CHUNKED>
+// ALL_SPLITS (S <= kMergeBatch): each wave takes one group of four columns
+// (q4 = its index) and every split, so no wave waits for another; the grid is
+// a quarter of the size.
+template <int D, int G, bool CHUNKED, bool ALL_SPLITS>
 __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(const TiledMergeArgs a) {
     constexpr int NSL = Cfg<D, G>::NSL, NT32 = Cfg<D, G>::NT32, ROWS = 16 * G;
     __shared__ float xch[kMergeWaves - 1][6][64];
-    // blockIdx.x = (r * NSL + v) * 4 + q4, blockIdx.y = kv head, blockIdx.z = request
-    const int q4 = blockIdx.x % 4;
-    const int v = (blockIdx.x / 4) % NSL;
-    const int r = blockIdx.x / (4 * NSL);
+    // blockIdx.x = (r * NSL + v) * 4 + q4 (ALL_SPLITS: r * NSL + v, q4 = wave),
+    // blockIdx.y = kv head, blockIdx.z = request
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int q4 = ALL_SPLITS ? wv : (int)(blockIdx.x % 4);
+    const int rv = ALL_SPLITS ? (int)blockIdx.x : (int)(blockIdx.x / 4);
+    const int v = rv % NSL;
+    const int r = rv / NSL;
     const int g = blockIdx.y, b = blockIdx.z;
     const BlockReq rq = block_req(a.draft_lens, nullptr, b, CHUNKED ? a.blocks_per_req : 1, a.T_max);
     const int lim = G * rq.dl;
     if (32 * r >= lim) return;                                // uniform: no row of this tile is a draft row
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int row = 32 * r + (lane & 31);
     const int S = a.num_splits;
     const int per = (S + kMergeWaves - 1) / kMergeWaves;
-    const int s_begin = min(S, wv * per), s_end = min(S, s_begin + per);
+    const int s_begin = ALL_SPLITS ? 0 : min(S, wv * per), s_end = ALL_SPLITS ? S : min(S, s_begin + per);
     const size_t blk0 = ((size_t)b * a.Hkv + g) * S;
     const uint16_t* src = a.part_h + blk0 * (ROWS * D) + (size_t)(((v * NT32 + r) * 4 + q4) * 64 + lane) * 4;
     const float* lse = a.part_hlse + blk0 * ROWS + row;
@@ -986,25 +991,27 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
         for (int u = 0; u < kMergeBatch; ++u)
             merge_fold(st, l[u], x[u], mn);
     }
-    if (wv > 0) {
-        xch[wv - 1][0][lane] = st.M;
-        xch[wv - 1][1][lane] = st.W;
+    if constexpr (!ALL_SPLITS) {
+        if (wv > 0) {
+            xch[wv - 1][0][lane] = st.M;
+            xch[wv - 1][1][lane] = st.W;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xch[wv - 1][2 + e][lane] = st.acc[e];
-    }
-    __syncthreads();
-    if (wv > 0) return;
+            for (int e = 0; e < 4; ++e) xch[wv - 1][2 + e][lane] = st.acc[e];
+        }
+        __syncthreads();
+        if (wv > 0) return;
 #pragma unroll
-    for (int k = 0; k < kMergeWaves - 1; ++k) {
-        const float Mk = xch[k][0][lane];
-        const float mn = fmaxf(st.M, Mk);
-        if (mn == -INFINITY) continue;
-        merge_rescale(st, mn);
-        // a wave without a live split holds W = 0 and acc = 0, and gets c = 0
-        const float c = __builtin_amdgcn_exp2f((Mk - mn) * 1.4426950408889634f);
-        st.W = __builtin_fmaf(c, xch[k][1][lane], st.W);
+        for (int k = 0; k < kMergeWaves - 1; ++k) {
+            const float Mk = xch[k][0][lane];
+            const float mn = fmaxf(st.M, Mk);
+            if (mn == -INFINITY) continue;
+            merge_rescale(st, mn);
+            // a wave without a live split holds W = 0 and acc = 0, and gets c = 0
+            const float c = __builtin_amdgcn_exp2f((Mk - mn) * 1.4426950408889634f);
+            st.W = __builtin_fmaf(c, xch[k][1][lane], st.W);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.acc[e] = __builtin_fmaf(c, xch[k][2 + e][lane], st.acc[e]);
+            for (int e = 0; e < 4; ++e) st.acc[e] = __builtin_fmaf(c, xch[k][2 + e][lane], st.acc[e]);
+        }
     }
     if (row >= lim) return;
     const float inv = st.W > 0.0f ? 1.0f / st.W : 0.0f;
@@ -1049,11 +1056,16 @@ template <int D, int G>
 static hipError_t launch_merge_tiled_dg(const TiledMergeArgs& a, hipStream_t stream) {
     if (a.B <= 0 || a.Hkv <= 0) return hipSuccess;
     if (a.B > 65535 || a.Hkv > 65535) return hipErrorInvalidConfiguration;
-    const dim3 grid(Cfg<D, G>::NT32 * Cfg<D, G>::NSL * 4, (unsigned)a.Hkv, (unsigned)a.B);
-    if (a.blocks_per_req > 1)
-        hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, true>), grid, dim3(kMergeWaves * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, false>), grid, dim3(kMergeWaves * 64), 0, stream, a);
+    const bool all = a.num_splits <= kMergeBatch;
+    const dim3 grid(Cfg<D, G>::NT32 * Cfg<D, G>::NSL * (all ? 1 : 4), (unsigned)a.Hkv, (unsigned)a.B);
+    const dim3 block(kMergeWaves * 64);
+    if (a.blocks_per_req > 1) {
+        if (all) hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (all) hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((splitk_merge_tiled_kernel<D, G, false, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
