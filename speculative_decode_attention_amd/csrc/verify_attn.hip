@@ -842,7 +842,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                     u32x2_t x;
                     x[0] = pack_f16x2(o[sl][r][4 * q4] * sc, o[sl][r][4 * q4 + 1] * sc);
                     x[1] = pack_f16x2(o[sl][r][4 * q4 + 2] * sc, o[sl][r][4 * q4 + 3] * sc);
-                    *reinterpret_cast<u32x2_t*>(dst + q4 * 256) = x;
+                    __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(dst + q4 * 256));
                 }
             }
         }
