@@ -26,6 +26,11 @@
  *  - Output of speculative decoding equals plain autoregressive decoding
  *    (discuss.pytorch.kr summary, DFlash 2 section).  At the attention level:
  *    row t of a block equals a one-token decode at context position t.
+ *  - Beside the causal block: tree-shaped block masks and sliding windows
+ *    (same section; see the functions below), greedy acceptance of the drafts
+ *    with the rollback of context_lens (same section), and prefill, whose
+ *    attention is this same definition with a block of any length (the
+ *    summary's Metal-kernels section keeps prefill and verify kernels apart).
  *
  * The pages give no formula, layout or precision.  Readings taken where they
  * are silent (all stated again in the design notes):
@@ -356,6 +361,11 @@ int splash_ref_verify_attn(const uint16_t* q, double* out,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, sm_scale, NULL, 0);
 }
 
+/* splash_ref_verify_attn_masked: block attention where draft t sees every key
+ * before the block and the block key of draft u only if bit u of
+ * block_masks[b][t] is set: a tree of candidate tokens per position, which the
+ * path selector of DFlash 2 chooses among (discuss.pytorch.kr summary, DFlash 2
+ * section); the chain mask (bits 0..t) is the causal block. */
 int splash_ref_verify_attn_masked(const uint16_t* q, double* out,
                                   const int8_t* k_pool, const int8_t* v_pool,
                                   const uint16_t* k_scale, const uint16_t* v_scale,
@@ -371,7 +381,9 @@ int splash_ref_verify_attn_masked(const uint16_t* q, double* out,
 }
 
 /* splash_ref_verify_attn_window: causal block attention where draft t at
- * position pos_t sees only keys pos_t - window < j <= pos_t (window >= 1). */
+ * position pos_t sees only keys pos_t - window < j <= pos_t (window >= 1): the
+ * draft model's sliding-window attention that bounds its memory
+ * (discuss.pytorch.kr summary, DFlash 2 section). */
 int splash_ref_verify_attn_window(const uint16_t* q, double* out,
                                   const int8_t* k_pool, const int8_t* v_pool,
                                   const uint16_t* k_scale, const uint16_t* v_scale,
