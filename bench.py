@@ -318,10 +318,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",                                  # MFMA operands (fp32 accumulation); q/out are bf16
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "global_batch": B, "seq_len": ctx, "draft_block": T,
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8",
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8", "io_dtype": "bf16",
                    "splits": S, "replicas": R, "calls_per_graph": C, "step_bytes": step_bytes,
                    "verify_us_per_call": round(us_verify, 2),
                    "verify_tree_mask_us_per_call": round(us_tree, 2),
