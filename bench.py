@@ -81,6 +81,7 @@ def parse():
                     help=f"also run a plain {CALIB_MIB} MiB device copy (for counter calibration)")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
     ap.add_argument("--summarize-traffic", nargs="+", metavar="ARG")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG")
     ap.add_argument("--oracle-one-thread", metavar="DIR", help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -124,6 +125,8 @@ def main():
         return summarize_stats(args.summarize_stats[0], args.summarize_stats[1:])
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic[:2], args.summarize_traffic[2:])
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters[0], args.summarize_counters[1:])
     if args.oracle_one_thread:
         return oracle_one_thread_child(args.oracle_one_thread)
     if args.gpus != 1:
@@ -838,6 +841,50 @@ def summarize_traffic(fetch_dir, write_dir, cmd):
               f"{fb / 1e6:.2f} | {wb / 1e6:.2f} |")
     print("\nRecord read by bench.py (`roofline.traffic`, only while the source hash matches):\n")
     print(json.dumps(rec))
+
+
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+               "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(d, cmd, n_cu=256, n_xcd=8):
+    """Markdown summary of one `rocprofv3 --pmc` pass of SQ counters over the
+    partition kernel's launches of the 32K workload (the shared-prefix and
+    context-scaling legs, which run last, are left out)."""
+    rows = sorted(csv.DictReader(open(_find(d, "counter_collection.csv"))), key=lambda r: int(r["Dispatch_Id"]))
+    per = {}
+    for r in rows:
+        if PART_KERNEL in r["Kernel_Name"]:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    drop = shared_leg_launches(PMC_STEPS) + scaling_leg_launches(PMC_STEPS)
+    mean = {k: float(np.mean(v[:-drop])) for k, v in per.items()}
+    n = len(next(iter(per.values()))) - drop
+    print("# SQ counters: verify partition kernel, 32K context, T=16, 24q/4kv heads, D=256\n")
+    print("Command (from the repository root on an MI355X), one pass:\n")
+    print("```\n" + " ".join(cmd) + "\n```\n")
+    print(f"Partition kernel source hash: `{kernel_source_hash()}`; {n} launches of the 32K workload "
+          "(mean per dispatch, summed over the device).\n")
+    print("| counter | mean per launch |")
+    print("|---|---:|")
+    for k in SQ_COUNTERS:
+        if k in mean:
+            print(f"| `{k}` | {mean[k]:.4g} |")
+    gui = mean.get("GRBM_GUI_ACTIVE")
+    mfma = mean.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    conf, lds = mean.get("SQ_LDS_BANK_CONFLICT"), mean.get("SQ_LDS_IDX_ACTIVE")
+    print("\nDerived:\n")
+    if gui and mfma is not None:
+        cyc = gui / n_xcd                                 # GRBM_GUI_ACTIVE is summed over the XCDs
+        print(f"- launch length: `GRBM_GUI_ACTIVE / {n_xcd} XCDs` = {cyc:.4g} cycles")
+        print(f"- MFMA busy: `SQ_VALU_MFMA_BUSY_CYCLES / (launch length x {n_cu} CUs x 4 SIMDs)` = "
+              f"{100 * mfma / (cyc * n_cu * 4):.1f}% of the launch's SIMD-cycles")
+    mops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F16")
+    if mops is not None:
+        print(f"- fp16 MFMA work: `SQ_INSTS_VALU_MFMA_MOPS_F16 x 512` = {mops * 512 / 1e9:.2f} GFLOP per launch "
+              "(the algorithmic 12.9 GFLOP plus the padded rows and the bias products)")
+    if lds:
+        print(f"- LDS bank conflicts: `SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE` = {100 * conf / lds:.2f}% of the LDS "
+              "active cycles")
 
 
 if __name__ == "__main__":
