@@ -226,7 +226,9 @@ struct Cfg {
 template <int D>
 __device__ __forceinline__ int k_swizzle(int slot) {
     constexpr int CH = D / 16;
-    return CH >= 8 ? (slot & 7) : ((slot / (8 / CH)) % CH);
+    // the LDS serves 16 lanes of a 16-byte read per cycle (64 banks): with 16
+    // chunks a row, the 16 rows of a page take 16 different chunk offsets
+    return CH >= 16 ? (slot & 15) : CH >= 8 ? (slot & 7) : ((slot / (8 / CH)) % CH);
 }
 
 // The body for NTU row tiles in use (NH = ceil(NTU / 2) per row half; a tile
