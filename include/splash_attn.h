@@ -62,20 +62,16 @@
  *  - Compiled shapes: P = 16; (D, Hq/Hkv) in {(64, 4), (128, 8), (256, 6)};
  *    T_max <= 16 for verify.  Append accepts D in {64, 128, 256} and any T_max.
  *  - q, out, k_pool, v_pool and the workspace must be 16-byte aligned.
- *  - Split partials (splash_verify_attn_partition / _splitk_merge, and the
- *    workspace of splash_verify_attn) use one layout.  With G = Hq / Hkv, a
- *    (request b, kv head g, split s) owns a block of 16 G rows, row
- *    r = t * G + (h - g G) for draft t of query head h:
- *      part_o   fp16  [B][Hkv][S][16 G * D]  each block stored as MFMA tiles
- *                     [c][R][q][l][e]: c < D / 32 slices of 32 columns,
- *                     R < G / 2 tiles of 32 rows, q < 4, lane l < 64, e < 4;
- *                     element (row r, column d) is at row 32 R + l % 32,
- *                     d = 32 c + 8 q + 4 (l / 32) + e
- *      part_lse fp32  [B][Hkv][S][16 G]  natural log
- *    Each block's rows are the normalised partial o_s scaled by 2^-k and its
- *    log-sum-exp raised by k ln 2 (k >= 0 chosen per block from its largest V
- *    scale so that fp16 holds o_s * 2^-k); e^lse * o, which the merge uses, is
- *    unchanged.  Rows r >= G * draft_lens[b] are neither written nor read.
+ *  - Split partials of splash_verify_attn_partition and
+ *    splash_verify_attn_splitk_merge (the exported pair, for callers that run
+ *    context splits themselves, e.g. one split per device), in fp32 rows:
+ *      part_o   fp32  [B][Hq][T_max][S][D]  the normalised partial row o_s of
+ *                     draft t, query head h, split s
+ *      part_lse fp32  [B][Hq][T_max][S]     its natural-log log-sum-exp lse_s
+ *                     (-inf for a split with no visible key; its row is 0)
+ *    Rows t >= draft_lens[b] are neither written nor read.
+ *  - The workspace of splash_verify_attn is opaque: its size comes from
+ *    splash_verify_attn_workspace_bytes and its contents are the library's.
  */
 #ifndef SPLASH_ATTN_H
 #define SPLASH_ATTN_H
@@ -135,9 +131,10 @@ int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P
 /*
  * splash_verify_attn_workspace_bytes -- bytes of device workspace
  * splash_verify_attn needs for num_splits splits (0 when num_splits <= 1): the
- * split partials in the layout above (fp16 part_o for B * 16 Hq rows per
- * split) followed, at a 256-byte aligned offset, by their fp32 part_lse.
- * T_max does not change the size.
+ * split partials, held as fp16 tiles in the order the kernels produce them
+ * (each (request, kv head, split) block scaled by a power of two that is folded
+ * into its log-sum-exp), followed, at a 256-byte aligned offset, by their fp32
+ * log-sum-exps.  T_max does not change the size.
  */
 size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits);
 
@@ -156,7 +153,9 @@ size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int n
  * one split runs, workspace must hold splash_verify_attn_workspace_bytes(...)
  * bytes (workspace may be NULL when one split runs).  Accumulation is in fp32
  * (split partials pass through fp16, a relative rounding of at most 2^-11);
- * the result is deterministic for a given num_splits.
+ * the result is deterministic for a given num_splits.  With more than one
+ * split, B and Hkv must be at most 65535 (else SPLASH_ERR_UNSUPPORTED, checked
+ * before anything is launched).
  */
 int splash_verify_attn(const uint16_t* q, uint16_t* out,
                        const int8_t* k_pool, const int8_t* v_pool,
@@ -256,12 +255,15 @@ size_t splash_prefill_attn_workspace_bytes(int B, int T_max, int Hq, int Hkv, in
  * L = splash_verify_attn_split_pages(...)), write for draft t < draft_lens[b]
  * and query head h the normalised partial row and its log-sum-exp
  *     o_s   = sum_{j in split, j <= pos_t} e^(z_j - m_s) v_hat_j / l_s
- *     lse_s = m_s + ln l_s      (natural log; -inf when the split holds no
- *                                visible key, and then its row is not written)
- * into part_o (fp16) and part_lse in the split-partial layout described at the
- * top of this header.  For callers that combine partials themselves (for
- * example across devices) with splash_verify_attn_splitk_merge.  num_splits
- * must be >= 1 (no preset here); the buffers use exactly num_splits as S.
+ *     lse_s = m_s + ln l_s      (natural log; -inf and a zero row when the
+ *                                split holds no visible key)
+ * into part_o and part_lse, fp32 rows in the layout described at the top of
+ * this header ([B][Hq][T_max][S][D] and [B][Hq][T_max][S], S = num_splits).
+ * For callers that combine partials themselves (for example across devices,
+ * each running the splits of its own page range) with
+ * splash_verify_attn_splitk_merge.  num_splits must be >= 1 (no preset here).
+ * part_o 16-byte aligned.  The fp16 roundings of p and p * v_scale inside the
+ * kernel are as in splash_verify_attn; the rows themselves are not rounded.
  */
 int splash_verify_attn_partition(const uint16_t* q,
                                  const int8_t* k_pool, const int8_t* v_pool,
@@ -270,7 +272,7 @@ int splash_verify_attn_partition(const uint16_t* q,
                                  const int32_t* context_lens, const int32_t* draft_lens,
                                  int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
                                  int max_context_len, float sm_scale, int num_splits,
-                                 uint16_t* part_o, float* part_lse, void* stream);
+                                 float* part_o, float* part_lse, void* stream);
 
 /*
  * splash_verify_attn_split_pages -- pages per split L that the partition uses
@@ -282,19 +284,19 @@ int splash_verify_attn_split_pages(int max_context_len, int P, int num_splits);
 
 /*
  * splash_verify_attn_splitk_merge -- combine S context splits by their
- * log-sum-exps: for draft t < draft_lens[b] and query head h (row r of kv head
- * g = h / (Hq/Hkv) in the split-partial layout),
+ * log-sum-exps: for draft t < draft_lens[b] and query head h,
  *     M = max_s lse_s,  w_s = e^(lse_s - M)
  *     out[b][t][h][:] = bf16( sum_s w_s o_s[:] / sum_s w_s )
- * folded in a fixed order that depends only on S (the result is
- * deterministic: the same inputs give the same bits); splits with lse = -inf
- * weigh nothing: their rows may be read (they must lie inside part_o) but
- * never reach the result, whatever they hold.  Rows t >= draft_lens[b] of out
- * are left untouched.  T_max <= 16 and (D, Hq/Hkv) in the compiled set.
+ * with part_o fp32 [B][Hq][T_max][S][D] (16-byte aligned) and part_lse fp32
+ * [B][Hq][T_max][S] as splash_verify_attn_partition writes them, out bf16
+ * [B][T_max][Hq][D] (8-byte aligned).  Splits are folded in ascending order, so
+ * the same inputs give the same bits; a split with lse = -inf weighs nothing,
+ * whatever its row holds.  Rows t >= draft_lens[b] of out are left untouched.
+ * D in {64, 128, 256}; any T_max and Hq.
  */
-int splash_verify_attn_splitk_merge(const uint16_t* part_o, const float* part_lse,
+int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse,
                                     uint16_t* out, const int32_t* draft_lens,
-                                    int B, int T_max, int Hq, int Hkv, int D, int num_splits,
+                                    int B, int T_max, int Hq, int D, int num_splits,
                                     void* stream);
 
 /*

@@ -86,7 +86,7 @@ def load_library(path: Path | None = None):
     lib.splash_verify_attn_partition.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                  _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P]
     lib.splash_verify_attn_split_pages.argtypes = [_I, _I, _I]
-    lib.splash_verify_attn_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    lib.splash_verify_attn_splitk_merge.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
     lib.splash_verify_accept_workspace_bytes.argtypes = [_I, _I, _I]
     lib.splash_verify_accept_workspace_bytes.restype = _Z
     lib.splash_verify_accept.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _Z, _P]
@@ -306,26 +306,25 @@ def _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
     return out
 
 
-def partial_shapes(B, Hq, Hkv, D, num_splits):
-    """Shapes of the split-partial buffers: part_o fp16 [B][Hkv][S][16 G * D] (MFMA
-    tile order inside a block) and part_lse fp32 [B][Hkv][S][16 G], G = Hq / Hkv."""
-    G = Hq // Hkv
-    return (B, Hkv, num_splits, 16 * G * D), (B, Hkv, num_splits, 16 * G)
+def partial_shapes(B, Hq, T_max, D, num_splits):
+    """Shapes of the exported split partials: part_o fp32 [B][Hq][T_max][S][D] and
+    part_lse fp32 [B][Hq][T_max][S]."""
+    return (B, Hq, T_max, num_splits, D), (B, Hq, T_max, num_splits)
 
 
 def splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                                  draft_lens, max_context_len, sm_scale, num_splits, part_o,
                                  part_lse, stream=None):
-    """Partial rows per context split into part_o (fp16 bits, shapes from
-    partial_shapes) and part_lse (fp32)."""
+    """Normalised partial rows and log-sum-exps per context split into part_o and
+    part_lse (fp32, shapes from partial_shapes)."""
     torch = _torch()
     B, T_max, Hq, Dq = q.shape
     _dev(q, "q", (torch.bfloat16, torch.int16))
     num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
     maxp = _lens(block_table, context_lens, draft_lens, B)
     S = int(num_splits)
-    po_shape, pl_shape = partial_shapes(B, Hq, Hkv, D, S)
-    _dev(part_o, "part_o", (torch.float16, torch.int16), po_shape)
+    po_shape, pl_shape = partial_shapes(B, Hq, T_max, D, S)
+    _dev(part_o, "part_o", (torch.float32,), po_shape)
     _dev(part_lse, "part_lse", (torch.float32,), pl_shape)
     rc = _lib().splash_verify_attn_partition(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
@@ -336,22 +335,21 @@ def splash_verify_attn_partition(q, k_pool, v_pool, k_scale, v_scale, block_tabl
 
 
 def splash_verify_attn_splitk_merge(part_o, part_lse, out, draft_lens, stream=None):
-    """Merge S splits (layout of partial_shapes) -> out [B][T_max][Hq][D] bf16."""
+    """Merge S splits (fp32 [B][Hq][T_max][S][D] rows and [B][Hq][T_max][S]
+    log-sum-exps) -> out [B][T_max][Hq][D] bf16."""
     torch = _torch()
     B, T_max, Hq, D = out.shape
     _dev(out, "out", (torch.bfloat16, torch.int16))
-    if part_lse.dim() != 4 or part_lse.shape[0] != B:
-        raise ValueError("part_lse must be [B][Hkv][S][16 G]")
-    Hkv, S = int(part_lse.shape[1]), int(part_lse.shape[2])
-    if Hkv <= 0 or Hq % Hkv:
-        raise ValueError("Hq must be a multiple of the kv head count")
-    po_shape, pl_shape = partial_shapes(B, Hq, Hkv, D, S)
-    _dev(part_o, "part_o", (torch.float16, torch.int16), po_shape)
+    if part_lse.dim() != 4:
+        raise ValueError("part_lse must be [B][Hq][T_max][S]")
+    S = int(part_lse.shape[3])
+    po_shape, pl_shape = partial_shapes(B, Hq, T_max, D, S)
+    _dev(part_o, "part_o", (torch.float32,), po_shape)
     _dev(part_lse, "part_lse", (torch.float32,), pl_shape)
     _dev(draft_lens, "draft_lens", (torch.int32,), (B,))
     rc = _lib().splash_verify_attn_splitk_merge(part_o.data_ptr(), part_lse.data_ptr(),
                                                 out.data_ptr(), draft_lens.data_ptr(), B, T_max,
-                                                Hq, Hkv, D, S, _stream(stream))
+                                                Hq, D, S, _stream(stream))
     _check(rc, "splash_verify_attn_splitk_merge")
     return out
 
@@ -375,8 +373,8 @@ def splash_verify_accept(logits, block_tokens, draft_lens, context_lens, accepte
                     ("next_token", next_token)):
         _dev(t, name, (torch.int32,), (B,))
     need = splash_verify_accept_workspace_bytes(B, T_max, V)
-    if workspace is None:                                     # counters must start at zero
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=logits.device)
+    if workspace is None:                                     # no need to clear it
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
     _dev(workspace, "workspace", (torch.uint8,))
     rc = _lib().splash_verify_accept(logits.data_ptr(), block_tokens.data_ptr(), draft_lens.data_ptr(),
                                      context_lens.data_ptr(), accepted.data_ptr(), next_token.data_ptr(),

@@ -159,9 +159,9 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
     }
     const int L = pages_per_split(span, P, num_splits);
     const int S = ceil_div(ceil_div(span, P), L);                // splits that hold pages
-    VerifyArgs a{q, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, block_table,
-                 max_pages_per_seq, context_lens, draft_lens, items, T_max, Hq, Hkv, D, sm_scale, S, L,
-                 num_pages};
+    VerifyArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale,
+                 block_table, max_pages_per_seq, context_lens, draft_lens, items, T_max, Hq, Hkv, D,
+                 sm_scale, S, L, num_pages};
     a.block_masks = block_masks;
     a.window = window;
     a.blocks_per_req = nblk;
@@ -170,6 +170,9 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
         a.out = out;
         return launch_verify_partition(a, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
     }
+    // the merge's grid takes requests (or blocks) and kv heads on its 16-bit axes:
+    // refuse before anything is launched
+    if (items > 65535 || Hkv > 65535) return SPLASH_ERR_UNSUPPORTED;
     const size_t need = splash_verify_attn_workspace_bytes(items, prefill ? kMaxVerifyT : T_max, Hq, D, S);
     if (!workspace || !aligned16(workspace)) return SPLASH_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < need) return SPLASH_ERR_WORKSPACE_TOO_SMALL;
@@ -253,35 +256,33 @@ int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const 
                                  const int32_t* block_table, int max_pages_per_seq,
                                  const int32_t* context_lens, const int32_t* draft_lens, int B,
                                  int T_max, int Hq, int Hkv, int D, int P, int num_pages,
-                                 int max_context_len, float sm_scale, int num_splits, uint16_t* part_o,
+                                 int max_context_len, float sm_scale, int num_splits, float* part_o,
                                  float* part_lse, void* stream) {
     int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                                  draft_lens, max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages,
                                  max_context_len, sm_scale);
     if (rc != SPLASH_OK) return rc;
-    if (!part_o || !part_lse || !aligned16(part_o) || !aligned16(part_lse) || num_splits <= 0)
-        return SPLASH_ERR_INVALID_ARGUMENT;
+    if (!part_o || !part_lse || !aligned16(part_o) || num_splits <= 0) return SPLASH_ERR_INVALID_ARGUMENT;
     if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;
     const int L = pages_per_split(max_context_len, P, num_splits);
-    VerifyArgs a{q, nullptr, part_o, part_lse, k_pool, v_pool, k_scale, v_scale, block_table,
-                 max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D, sm_scale,
-                 num_splits, L, num_pages};
+    VerifyArgs a{q, nullptr, nullptr, nullptr, part_o, part_lse, k_pool, v_pool, k_scale, v_scale,
+                 block_table, max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D,
+                 sm_scale, num_splits, L, num_pages};
     return launch_verify_partition(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
                                                                                      : SPLASH_ERR_LAUNCH;
 }
 
-int splash_verify_attn_splitk_merge(const uint16_t* part_o, const float* part_lse, uint16_t* out,
-                                    const int32_t* draft_lens, int B, int T_max, int Hq, int Hkv, int D,
+int splash_verify_attn_splitk_merge(const float* part_o, const float* part_lse, uint16_t* out,
+                                    const int32_t* draft_lens, int B, int T_max, int Hq, int D,
                                     int num_splits, void* stream) {
     if (!part_o || !part_lse || !out || !draft_lens) return SPLASH_ERR_INVALID_ARGUMENT;
-    if (B < 0 || T_max < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_splits <= 0 || Hq % Hkv != 0)
-        return SPLASH_ERR_INVALID_ARGUMENT;
-    if (!aligned16(part_o) || !aligned16(out)) return SPLASH_ERR_INVALID_ARGUMENT;
-    if (T_max > kMaxVerifyT || !verify_supported(D, Hq / Hkv)) return SPLASH_ERR_UNSUPPORTED;
+    if (B < 0 || T_max < 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(out) & 7u)) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (!merge_rows_supported(D)) return SPLASH_ERR_UNSUPPORTED;
     if (B == 0 || T_max == 0) return SPLASH_OK;
-    TiledMergeArgs m{part_o, part_lse, out, draft_lens, B, T_max, Hq, Hkv, D, num_splits};
-    return launch_splitk_merge_tiled(m, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
-                                                                                      : SPLASH_ERR_LAUNCH;
+    RowMergeArgs m{part_o, part_lse, out, draft_lens, B, T_max, Hq, D, num_splits};
+    return launch_splitk_merge_rows(m, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
+                                                                                     : SPLASH_ERR_LAUNCH;
 }
 
 size_t splash_verify_accept_workspace_bytes(int B, int T_max, int V) {

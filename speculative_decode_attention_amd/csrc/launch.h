@@ -28,6 +28,8 @@ struct VerifyArgs {
     uint16_t* out;             // final bf16 rows (one split)            or nullptr
     uint16_t* part_h;          // fp16 tiled partial rows (several splits) or nullptr
     float* part_hlse;          // their natural-log log-sum-exps, [B][Hkv][S][16 G]
+    float* part_o32;           // or: fp32 partial rows [B][Hq][T_max][S][D] (the exported layout)
+    float* part_lse32;         //     and their natural-log log-sum-exps [B][Hq][T_max][S]
     const int8_t* k_pool;
     const int8_t* v_pool;
     const uint16_t* k_scale;
@@ -44,6 +46,16 @@ struct VerifyArgs {
     const uint32_t* block_masks = nullptr;   // [B][T_max] bit u of row t: draft t sees draft u; null: causal
     int window = 0;                          // > 0: draft at position p sees keys p - window < j <= p
     int blocks_per_req = 1;                  // > 1: a prefill chunk cut into 16-token blocks, B counts blocks
+};
+
+// Merge of fp32 partial rows in the exported layout: part_o [B][Hq][T_max][S][D],
+// part_lse [B][Hq][T_max][S] -> out bf16 [B][T_max][Hq][D].
+struct RowMergeArgs {
+    const float* part_o;
+    const float* part_lse;
+    uint16_t* out;
+    const int32_t* draft_lens;
+    int B, T_max, Hq, D, num_splits;
 };
 
 struct TiledMergeArgs {
@@ -77,6 +89,8 @@ bool verify_supported(int D, int G);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_verify_partition(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_splitk_merge_tiled(const TiledMergeArgs& a, hipStream_t stream);
+bool merge_rows_supported(int D);
+hipError_t launch_splitk_merge_rows(const RowMergeArgs& a, hipStream_t stream);
 int accept_num_chunks(int V);
 hipError_t launch_verify_accept(const AcceptArgs& a, hipStream_t stream);
 

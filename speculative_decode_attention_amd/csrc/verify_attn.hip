@@ -801,7 +801,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     // largest V scale of the split, so that |o| <= 127 * that scale * 2^-k stays
     // inside binary16; k goes into the log-sum-exp, which leaves e^lse * o unchanged
     int kshift = 0;
-    if (a.out == nullptr) {
+    if (a.out == nullptr && a.part_o32 == nullptr) {
         float vm = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) vm = fmaxf(vm, vtop[i]);
@@ -833,6 +833,17 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                            ((uint32_t)f32_to_bf16_rne(o[sl][r][4 * q4 + 3] * inv) << 16);
                     *reinterpret_cast<u32x2_t*>(orow + d) = x;
                 }
+            } else if (a.part_o32 != nullptr) {
+                // exported layout: fp32 rows [B][Hq][T_max][S][D], 16 bytes a lane
+                float* orow = a.part_o32 + ((((size_t)br * Hq + hq) * a.T_max + t_off + t) * S + s) * D;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * vs + 8 * q4 + 4 * (lane >> 5);
+                    f32x4_t x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = o[sl][r][4 * q4 + e] * inv;
+                    *reinterpret_cast<f32x4_t*>(orow + d) = x;
+                }
             } else {
                 // tile order [slice][32-row tile r][q4][lane][4]: every store of
                 // the wave writes 512 contiguous bytes
@@ -849,9 +860,14 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             }
         }
         if (a.out == nullptr && c == 0 && lane < 32) {
-            const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
             const float m = rowv[row];
-            a.part_hlse[blk * (16 * G) + row] = l > 0.0f ? (m + __builtin_log2f(l) + (float)kshift) * kLn2 : -INFINITY;
+            const float lse = l > 0.0f ? (m + __builtin_log2f(l) + (float)kshift) * kLn2 : -INFINITY;
+            if (a.part_o32 != nullptr) {
+                a.part_lse32[(((size_t)br * Hq + hq) * a.T_max + t_off + t) * S + s] = lse;
+            } else {
+                const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
+                a.part_hlse[blk * (16 * G) + row] = lse;
+            }
         }
     }
 }
@@ -892,9 +908,18 @@ void verify_partition_kernel(const VerifyArgs a) {
     const int pg_begin = lo_page + s * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_pages);
     const int rows = G * dl;
-    if (pg_begin >= pg_end) {                                 // empty split: mark it, write no row
-        for (int r = threadIdx.x; r < rows; r += kWaves * 64) {
-            a.part_hlse[(((size_t)b * a.Hkv + g) * S + s) * (16 * G) + r] = -INFINITY;
+    if (pg_begin >= pg_end) {                                 // empty split: lse = -inf
+        if (a.part_o32 != nullptr) {
+            // exported layout: the rows are written too (zero), as the definition gives
+            for (int i = threadIdx.x; i < rows * (D / 4); i += kWaves * 64) {
+                const int r = i / (D / 4), t = r / G, hq = g * G + r % G;
+                const size_t prow = (((size_t)rq.req * a.Hq + hq) * a.T_max + rq.t_off + t) * S + s;
+                reinterpret_cast<f32x4_t*>(a.part_o32 + prow * D)[i % (D / 4)] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (i % (D / 4) == 0) a.part_lse32[prow] = -INFINITY;
+            }
+        } else {
+            for (int r = threadIdx.x; r < rows; r += kWaves * 64)
+                a.part_hlse[(((size_t)b * a.Hkv + g) * S + s) * (16 * G) + r] = -INFINITY;
         }
         return;
     }
@@ -1023,6 +1048,92 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
     o[0] = (uint32_t)f32_to_bf16_rne(st.acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(st.acc[1] * inv) << 16);
     o[1] = (uint32_t)f32_to_bf16_rne(st.acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(st.acc[3] * inv) << 16);
     *reinterpret_cast<u32x2_t*>(a.out + (((size_t)rq.req * a.T_max + rq.t_off + t) * a.Hq + hq) * D + d) = o;
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of fp32 partial rows in the exported layout
+// (part_o [B][Hq][T_max][S][D], part_lse [B][Hq][T_max][S]).  D / 4 threads per
+// output row, 4 consecutive columns each (16-byte loads); a thread issues the
+// loads of kMergeBatch splits before folding them in split order, so the
+// result depends only on S.  Rows are numbered in the output's order
+// (b, t, h), so neighbouring threads of a workgroup write neighbouring rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void splitk_merge_rows_kernel(const RowMergeArgs a) {
+    constexpr int TPR = D / 4;                                // threads per output row
+    constexpr int RPB = 256 / TPR;                            // rows per workgroup
+    constexpr float kLog2e = 1.4426950408889634f;
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c4 = threadIdx.x % TPR;
+    if (row >= (long)a.B * a.T_max * a.Hq) return;
+    const int h = (int)(row % a.Hq);
+    const long bt = row / a.Hq;
+    const int t = (int)(bt % a.T_max), b = (int)(bt / a.T_max);
+    if (t >= min(a.draft_lens[b], a.T_max)) return;           // not a draft row: untouched
+    const int S = a.num_splits;
+    const size_t prow = (((size_t)b * a.Hq + h) * a.T_max + t) * (size_t)S;
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part_o + prow * D) + c4;
+    const float* lse = a.part_lse + prow;
+    float M = -INFINITY, W = 0.0f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+        f32x4_t x[kMergeBatch];
+        float l[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const int sp = min(s0 + u, S - 1);                // past the end: re-read, selected away
+            x[u] = src[(size_t)sp * TPR];
+            l[u] = lse[sp];
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            l[u] = s0 + u < S ? l[u] : -INFINITY;
+            mb = fmaxf(mb, l[u]);
+        }
+        const float mn = fmaxf(M, mb);
+        if (mn == -INFINITY) continue;                        // no split with a visible key yet
+        const float cr = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - mn) * kLog2e);
+        W *= cr;
+        acc *= cr;
+        M = mn;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            // an empty split weighs exp2(-inf) = 0 and its row, which may hold
+            // anything, is zeroed bitwise
+            const float wt = __builtin_amdgcn_exp2f((l[u] - mn) * kLog2e);
+            const uint32_t keep = l[u] != -INFINITY ? 0xffffffffu : 0u;
+            W += wt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[e] = __builtin_fmaf(wt, bit_cast<float>(bit_cast<uint32_t>(x[u][e]) & keep), acc[e]);
+        }
+    }
+    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    u32x2_t o;
+    o[0] = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
+    o[1] = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+    *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.T_max + t) * a.Hq + h) * D + 4 * c4) = o;
+}
+
+bool merge_rows_supported(int D) { return D == 64 || D == 128 || D == 256; }
+
+template <int D>
+static hipError_t launch_merge_rows_d(const RowMergeArgs& a, hipStream_t stream) {
+    constexpr int RPB = 256 / (D / 4);
+    const long rows = (long)a.B * a.T_max * a.Hq;
+    if (rows <= 0) return hipSuccess;
+    const long blocks = (rows + RPB - 1) / RPB;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((splitk_merge_rows_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_merge_rows(const RowMergeArgs& a, hipStream_t stream) {
+    if (a.D == 64) return launch_merge_rows_d<64>(a, stream);
+    if (a.D == 128) return launch_merge_rows_d<128>(a, stream);
+    if (a.D == 256) return launch_merge_rows_d<256>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

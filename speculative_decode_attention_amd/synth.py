@@ -113,7 +113,7 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
                   D: int, num_pages: int, P: int = 16, draft_lens=None, values: str = "quantized",
                   placement: str = "random", shared_prefix: int = 0, nan_pad_q: bool = False,
                   sm_scale: float | None = None, extra_pages: int = 0, k_mag: float = 1.0,
-                  v_mag: float = 1.0) -> Workload:
+                  v_mag: float = 1.0, k_spike=None) -> Workload:
     """Build one seeded workload.
 
     values: "quantized" -> fp32 N(0,1) K/V source rows appended through the
@@ -121,7 +121,14 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
     scales uniform in [0.01, 0.05] placed in the pools as given.
     draft_lens: a list, or "random" for uniform draws in 1..T_max.
     k_mag, v_mag: standard deviations of the "quantized" K and V source rows
-    (large values give peaked scores and V scales beyond fp16's room).
+    (large values give peaked scores; large or small V values give V scales far
+    from 1).
+    k_spike: None, or a function amp(pos, ctx) -> float array giving, for the
+    context positions pos of a request whose context holds ctx tokens, an
+    amplitude a; the K source row at pos gets a * w added, with w one N(0,1)
+    vector per kv head (drawn last, after the draft lengths).  Rising amplitudes
+    put a row's largest score late in the context ("quantized" values, no
+    shared prefix).
     shared_prefix: tokens (a whole number of pages) that every request shares
     through identical block-table entries.
     """
@@ -187,6 +194,14 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
         if dl.size == 1 and B > 1:
             dl = np.full(B, int(dl[0]), dtype=np.int32)
     assert all(0 <= d <= T_max and d <= c for d, c in zip(dl, ctx))
+
+    if k_spike is not None:
+        assert values == "quantized" and shared_prefix == 0, "K spikes take private quantised contexts"
+        w = rng.standard_normal((Hkv, D), dtype=np.float32)
+        for b in range(B):
+            start = sum(own[:b])
+            amp = np.asarray(k_spike(np.arange(own[b]), int(ctx[b])), dtype=np.float32)
+            k_all[start:start + own[b]] += amp[:, None, None] * w[None]
 
     if nan_pad_q:
         for b in range(B):

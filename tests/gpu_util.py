@@ -89,59 +89,6 @@ def assert_attn_ok(got, ref, where, mag=None):
     return e
 
 
-# ---- split-partial layout -------------------------------------------------
-# A (request b, kv head g, split s) block holds 16 G rows, row r = t G + (h - g G);
-# its fp16 values are stored in MFMA tile order [c][R][q][l][e] with element
-# (row 32 R + l % 32, column 32 c + 8 q + 4 (l // 32) + e).
-
-def _tile_axes(G, D):
-    return (D // 32, G // 2, 4, 2, 32, 4)          # c, R, q, l // 32, l % 32, e
-
-
-def untile_partials(po, G, D):
-    """po [..., 16 G * D] (fp16 bits) -> fp64 [..., 16 G, D] in row order."""
-    po = np.asarray(po).view(np.float16)
-    lead = po.shape[:-1]
-    x = po.reshape(lead + _tile_axes(G, D))
-    n = len(lead)
-    # -> R, l%32, c, q, l//32, e
-    x = x.transpose(tuple(range(n)) + (n + 1, n + 4, n + 0, n + 2, n + 3, n + 5))
-    return x.reshape(lead + (16 * G, D)).astype(np.float64)
-
-
-def tile_partials(o, G, D):
-    """fp [..., 16 G, D] -> fp16 bits [..., 16 G * D] in tile order."""
-    o = np.asarray(o, np.float16)
-    lead = o.shape[:-2]
-    n = len(lead)
-    x = o.reshape(lead + (G // 2, 32, D // 32, 4, 2, 4))      # R, l%32, c, q, l//32, e
-    x = x.transpose(tuple(range(n)) + (n + 2, n + 0, n + 3, n + 4, n + 1, n + 5))
-    return np.ascontiguousarray(x).reshape(lead + (16 * G * D,)).view(np.uint16)
-
-
-def blocks_to_heads(x, G, T_max):
-    """[B, Hkv, S, 16 G, ...] block rows -> [B, Hq, T_max, S, ...]."""
-    B, Hkv, S = x.shape[:3]
-    rest = x.shape[4:]
-    y = x.reshape((B, Hkv, S, 16, G) + rest)
-    y = np.moveaxis(y, 2, 4)                        # B, Hkv, 16, G, S, ...
-    y = np.moveaxis(y, 3, 2)                        # B, Hkv, G, 16, S, ...
-    return y.reshape((B, Hkv * G, 16, S) + rest)[:, :, :T_max]
-
-
-def heads_to_blocks(x, Hkv):
-    """[B, Hq, T, S, ...] -> [B, Hkv, S, 16 G, ...] (rows t >= T zero)."""
-    B, Hq, T, S = x.shape[:4]
-    rest = x.shape[4:]
-    G = Hq // Hkv
-    y = np.zeros((B, Hq, 16, S) + rest, x.dtype)
-    y[:, :, :T] = x
-    y = y.reshape((B, Hkv, G, 16, S) + rest)
-    y = np.moveaxis(y, 4, 2)                        # B, Hkv, S, G, 16, ...
-    y = np.swapaxes(y, 3, 4)                        # B, Hkv, S, 16, G, ...
-    return y.reshape((B, Hkv, S, 16 * G) + rest)
-
-
 class Prepared:
     """One workload with oracle pools (host) and GPU pools built by the GPU append."""
 

@@ -132,13 +132,23 @@ def test_append_empty_is_a_no_op(lib):
 
 
 def test_merge_rejects_bad_arguments(lib):
+    # (part_o, part_lse, out, draft_lens, B, T_max, Hq, D, num_splits, stream)
     m = lib.splash_verify_attn_splitk_merge
-    assert m(None, FAKE, FAKE, FAKE, 1, 16, 24, 4, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 4, 256, 0, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 5, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 4, 96, 4, None) == sda.SPLASH_ERR_UNSUPPORTED
-    assert m(FAKE, FAKE, FAKE, FAKE, 1, 17, 24, 4, 256, 4, None) == sda.SPLASH_ERR_UNSUPPORTED
-    assert m(FAKE, FAKE, FAKE, FAKE, 0, 16, 24, 4, 256, 4, None) == sda.SPLASH_OK
+    assert m(None, FAKE, FAKE, FAKE, 1, 16, 24, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, None, 1, 16, 24, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 256, 0, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE + 8, FAKE, FAKE, FAKE, 1, 16, 24, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE + 4, FAKE, 1, 16, 24, 256, 4, None) == sda.SPLASH_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 16, 24, 96, 4, None) == sda.SPLASH_ERR_UNSUPPORTED
+    assert m(FAKE, FAKE, FAKE, FAKE, 0, 16, 24, 256, 4, None) == sda.SPLASH_OK
+    assert m(FAKE, FAKE, FAKE, FAKE, 1, 0, 24, 256, 4, None) == sda.SPLASH_OK
+
+
+def test_verify_refuses_merge_grids_it_cannot_launch(lib):
+    """More than 65535 requests with several splits is refused before anything is
+    launched (the pointers are never dereferenced, so nothing ran)."""
+    assert _verify(lib, B=65536, S=64, ws=FAKE, ws_bytes=1 << 40) == sda.SPLASH_ERR_UNSUPPORTED
+    assert _verify(lib, B=65536, S=64, ws=None) == sda.SPLASH_ERR_UNSUPPORTED
 
 
 def test_partition_rejects_bad_arguments(lib):
