@@ -131,10 +131,11 @@ int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P
 /*
  * splash_verify_attn_workspace_bytes -- bytes of device workspace
  * splash_verify_attn needs for num_splits splits (0 when num_splits <= 1): the
- * split partials, held as fp16 tiles in the order the kernels produce them
- * (each (request, kv head, split) block scaled by a power of two that is folded
- * into its log-sum-exp), followed, at a 256-byte aligned offset, by their fp32
- * log-sum-exps.  T_max does not change the size.
+ * split partials, held as fp16 tiles in the order the kernels produce them,
+ * each (request, kv head, split) block holding its rows times a power of two
+ * 2^jv chosen from its V scales (so that small and large V values both keep
+ * binary16's precision), then, at 256-byte aligned offsets, their fp32
+ * log-sum-exps and one int32 jv per block.  T_max does not change the size.
  */
 size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits);
 

@@ -128,9 +128,11 @@ int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P
 size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int num_splits) {
     if (B <= 0 || T_max <= 0 || Hq <= 0 || D <= 0 || num_splits <= 1) return 0;
     // tiled fp16 partials for 16 drafts of every query head (B * Hkv * 16 G rows
-    // per split = B * 16 Hq), then fp32 log-sum-exps
+    // per split = B * 16 Hq), then fp32 log-sum-exps, then one int32 V exponent
+    // per (request, kv head, split) block (B * Hq * S bounds B * Hkv * S)
     const size_t rows = (size_t)B * 16 * Hq * num_splits;
-    return align_up(rows * D * 2, 256) + align_up(rows * sizeof(float), 256);
+    return align_up(rows * D * 2, 256) + align_up(rows * sizeof(float), 256) +
+           align_up((size_t)B * Hq * num_splits * sizeof(int), 256);
 }
 
 static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
@@ -159,9 +161,9 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
     }
     const int L = pages_per_split(span, P, num_splits);
     const int S = ceil_div(ceil_div(span, P), L);                // splits that hold pages
-    VerifyArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale,
-                 block_table, max_pages_per_seq, context_lens, draft_lens, items, T_max, Hq, Hkv, D,
-                 sm_scale, S, L, num_pages};
+    VerifyArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, k_pool, v_pool, k_scale,
+                 v_scale, block_table, max_pages_per_seq, context_lens, draft_lens, items, T_max, Hq, Hkv,
+                 D, sm_scale, S, L, num_pages};
     a.block_masks = block_masks;
     a.window = window;
     a.blocks_per_req = nblk;
@@ -179,8 +181,10 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
     const size_t rows = (size_t)items * 16 * Hq * S;
     a.part_h = static_cast<uint16_t*>(workspace);
     a.part_hlse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * D * 2, 256));
+    a.part_hjv = reinterpret_cast<int*>(static_cast<char*>(workspace) + align_up(rows * D * 2, 256) +
+                                        align_up(rows * sizeof(float), 256));
     if (launch_verify_partition(a, st) != hipSuccess) return SPLASH_ERR_LAUNCH;
-    TiledMergeArgs m{a.part_h, a.part_hlse, out, draft_lens, items, T_max, Hq, Hkv, D, S};
+    TiledMergeArgs m{a.part_h, a.part_hlse, a.part_hjv, out, draft_lens, items, T_max, Hq, Hkv, D, S};
     m.blocks_per_req = nblk;
     return launch_splitk_merge_tiled(m, st) == hipSuccess ? SPLASH_OK : SPLASH_ERR_LAUNCH;
 }
@@ -265,8 +269,8 @@ int splash_verify_attn_partition(const uint16_t* q, const int8_t* k_pool, const 
     if (!part_o || !part_lse || !aligned16(part_o) || num_splits <= 0) return SPLASH_ERR_INVALID_ARGUMENT;
     if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;
     const int L = pages_per_split(max_context_len, P, num_splits);
-    VerifyArgs a{q, nullptr, nullptr, nullptr, part_o, part_lse, k_pool, v_pool, k_scale, v_scale,
-                 block_table, max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D,
+    VerifyArgs a{q, nullptr, nullptr, nullptr, nullptr, part_o, part_lse, k_pool, v_pool, k_scale,
+                 v_scale, block_table, max_pages_per_seq, context_lens, draft_lens, B, T_max, Hq, Hkv, D,
                  sm_scale, num_splits, L, num_pages};
     return launch_verify_partition(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SPLASH_OK
                                                                                      : SPLASH_ERR_LAUNCH;

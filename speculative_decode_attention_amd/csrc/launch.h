@@ -28,6 +28,7 @@ struct VerifyArgs {
     uint16_t* out;             // final bf16 rows (one split)            or nullptr
     uint16_t* part_h;          // fp16 tiled partial rows (several splits) or nullptr
     float* part_hlse;          // their natural-log log-sum-exps, [B][Hkv][S][16 G]
+    int* part_hjv;             // each block's V exponent: the tiles hold the rows times 2^jv, [B][Hkv][S]
     float* part_o32;           // or: fp32 partial rows [B][Hq][T_max][S][D] (the exported layout)
     float* part_lse32;         //     and their natural-log log-sum-exps [B][Hq][T_max][S]
     const int8_t* k_pool;
@@ -61,6 +62,7 @@ struct RowMergeArgs {
 struct TiledMergeArgs {
     const uint16_t* part_h;
     const float* part_hlse;
+    const int* part_hjv;
     uint16_t* out;
     const int32_t* draft_lens;
     int B, T_max, Hq, Hkv, D, num_splits;

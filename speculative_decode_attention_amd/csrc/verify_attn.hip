@@ -275,7 +275,8 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     auto last_step = [&](int p) -> int { return (pg_end - pg_begin - 1 - p) >> 2; };
     float* const red = reinterpret_cast<float*>(lds + C::M_OFF);     // [row][page pair]
     float* const rowv = reinterpret_cast<float*>(lds + C::R_OFF);
-    float* const vtop = reinterpret_cast<float*>(lds + C::F_OFF);    // after the loop: V scale maxima
+    float* const vxch = reinterpret_cast<float*>(lds + C::F_OFF + 32);   // [score wave] step V-scale maxima
+    int* const jv_out = reinterpret_cast<int*>(lds + C::F_OFF + 48);     // after the loop: the V exponent
     // flags of step j: one byte per score wave (bytes 4-7 stay zero)
     auto read_flags = [&](int j) -> uint32_t {
         const u32x2_t fl = *reinterpret_cast<const u32x2_t*>(lds + C::F_OFF + (j & 1) * kWaves);
@@ -424,17 +425,49 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 for (int i = 0; i < NH; ++i) nqb[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qf[kb][i], nqb[i], 0, 0, 0);
         }
         // per-row state of this half's tiles (row 16 (t0 + i) + li, the same in all lanes of a row)
-        float m_ref[NH], nmr[NH], l_run[NH], thr[NH];
+        // nmr = minus the row's reference (0 until it has one).  hasref: bit
+        // 16 i + li is set once row 16 (t0 + i) + li has a reference (a scalar
+        // mask: every lane of a row agrees on it, and it costs no VGPR)
+        float nmr[NH], l_run[NH];
+        uint64_t hasref = 0;
+        auto has_ref = [&](int i) -> bool {
+            const uint32_t f = __builtin_amdgcn_readfirstlane((uint32_t)(hasref >> (16 * i)) & 0xffffu);
+            return ((f >> li) & 1u) != 0;
+        };
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
-            m_ref[i] = -INFINITY;                             // no key seen yet
-            nmr[i] = 0.0f;                                    // -(m_ref if finite, else 0)
+            nmr[i] = 0.0f;
             l_run[i] = 0.0f;
-            thr[i] = -INFINITY;                               // -inf until the row has a reference, then tau
         }
         f32x4_t zs[2][NH];                                    // scores of the previous step, relative to m
         f16x2_t vsh[2][2];                                    // V scales of the previous step's keys (fp16 pairs)
-        f16x2_t vmax2 = {(_Float16)0.0f, (_Float16)0.0f};     // largest V scales of any key this lane scored
+        // V exponent: the softmax weights are carried as p 2^jv (fp32), and
+        // P' = p 2^jv s_v is rounded to binary16 once, with jv chosen so that the
+        // largest V scale seen so far, times 2^jv, lies in [64, 128): with
+        // p <= 2^tau, P' stays below 2^15, and P' of small V scales or small p
+        // stays normal.  The row sums carry the same 2^jv, so O / l is the row.
+        // A step holding a scale at or above vlim = 2^(7 - jv) (the next binade)
+        // raises the wave's flag, and the exchange lowers jv for every wave (the
+        // row sums and O are rescaled by the same power of two).  Until a nonzero
+        // scale is seen, jv = 0 and vlim is the least positive normal float.
+        // Identical in every score wave: set only from maxima all of them read.
+        int jv = 0;
+        float jvf = 0.0f, vlim = 1.17549435e-38f, vrun = 0.0f;   // vrun: largest V scale seen
+        // this lane's largest V scale among the keys of the last scored step (its
+        // pages' scales stay in vsh until the next step is scored; 0 past the context)
+        auto vscale_max = [&]() -> float {
+            const f16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(vsh[0][0], vsh[0][1]),
+                                                         __builtin_elementwise_max(vsh[1][0], vsh[1][1]));
+            return fmaxf((float)m2[0], (float)m2[1]);
+        };
+        auto set_jv = [&](float m) {                          // m > 0, uniform: the largest V scale
+            const uint32_t mb = __builtin_amdgcn_readfirstlane(bit_cast<uint32_t>(m));
+            vrun = bit_cast<float>(mb);
+            const int e = (int)((mb >> 23) & 0xffu) - 127;    // floor(log2 m), m normal in fp32
+            jv = 6 - e;
+            jvf = (float)jv;
+            vlim = bit_cast<float>((uint32_t)(e + 1 + 127) << 23);   // 2^(e + 1)
+        };
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -451,13 +484,13 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             const bool do_sm = it >= 1 && it <= n;
             const uint32_t flags = do_sm ? read_flags(it - 1) : 0u;
             // ---- references.  A flag says some score of the wave's pages
-            // exceeded the row's reference by more than the slack (bit 0), and
-            // whether a V scale of them exceeds 255 (bit 1).  Without bit 0
-            // anywhere no reference moves: every p <= 2^slack and P' stays inside
-            // fp16.  Otherwise the exact step maxima are exchanged, the rows
-            // beyond the step's slack move to them and the output waves rescale O.
+            // exceeded the row's reference by more than the slack, or a V scale
+            // reached vlim.  Without a flag anywhere nothing moves: every
+            // p <= 2^slack and P' stays inside binary16.  Otherwise the exact step
+            // maxima (scores per row, V scales per wave) are exchanged, the rows
+            // beyond the slack move to their maxima, jv follows the V scales, and
+            // the output waves rescale O.
             if (flags & 1u) {                                 // rare after the first step
-                const float tau = (flags & 2u) ? 0.0f : kTau;
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const f32x4_t z0 = zs[0][i], z1 = zs[1][i];
@@ -466,38 +499,58 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                     const float mx = group4_max(m4);
                     if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = mx;
                 }
+                {
+                    const float vw = wave_max(vscale_max());
+                    if (lane == 0) vxch[v] = vw;
+                }
                 lds_barrier();
+                // the O factor of a V-exponent change is an exact power of two (a
+                // rise of jv only happens while every scale seen was 0, so O = 0)
+                float vscale = 1.0f;
+                {
+                    const float vnew = bit_cast<float>(__builtin_amdgcn_readfirstlane(
+                        bit_cast<uint32_t>(fmaxf(fmaxf(vxch[0], vxch[1]), fmaxf(vxch[2], vxch[3])))));
+                    if (vnew >= vlim) {
+                        const int old = jv;
+                        set_jv(fmaxf(vrun, vnew));
+                        vscale = __builtin_ldexpf(1.0f, jv - old);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const u32x2_t mw = *reinterpret_cast<const u32x2_t*>(red + (16 * (t0 + i) + li) * 2);
                     const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));
-                    const bool fresh = m_ref[i] == -INFINITY;
-                    const bool move = fresh ? mstep > -INFINITY : mstep > tau;
+                    const bool fresh = !has_ref(i);
+                    const bool move = fresh ? mstep > -INFINITY : mstep > kTau;
                     float alpha = 1.0f;
                     if (move) {
                         alpha = fresh ? 0.0f : __builtin_amdgcn_exp2f(-mstep);
-                        m_ref[i] = (fresh ? 0.0f : m_ref[i]) + mstep;
-                        nmr[i] = -m_ref[i];
-                        thr[i] = kTau;
-                        l_run[i] *= alpha;
+                        nmr[i] -= mstep;                      // a fresh row has nmr = 0
+                        l_run[i] *= alpha;                    // (the V factor below as well)
 #pragma unroll
                         for (int k = 0; k < 2; ++k)
 #pragma unroll
                             for (int j = 0; j < 4; ++j) zs[k][i][j] -= mstep;
                     }
-                    if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = alpha;
+                    l_run[i] *= vscale;
+                    if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = alpha * vscale;
+                    hasref |= (__builtin_amdgcn_ballot_w64(move) & 0xffffull) << (16 * i);   // lanes gq = 0
                 }
                 lds_barrier();                                // factors written, maxima read
             }
-            if (it == 1) {                                    // first references (O is still zero)
+            if (it == 1) {                                    // first references and V exponent (O is still zero)
+                {
+                    const float v0 = bit_cast<float>(__builtin_amdgcn_readfirstlane(
+                        bit_cast<uint32_t>(fmaxf(fmaxf(vxch[0], vxch[1]), fmaxf(vxch[2], vxch[3])))));
+                    if (v0 > 0.0f) set_jv(v0);
+                }
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const u32x2_t mw = *reinterpret_cast<const u32x2_t*>(red + (16 * (t0 + i) + li) * 2);
                     const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));
+                    hasref |= (__builtin_amdgcn_ballot_w64(mstep > -INFINITY) & 0xffffull) << (16 * i);
                     if (mstep > -INFINITY) {
-                        m_ref[i] = mstep;
                         nmr[i] = -mstep;
-                        thr[i] = kTau;
 #pragma unroll
                         for (int k = 0; k < 2; ++k)
 #pragma unroll
@@ -515,17 +568,16 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const int t = t0 + i;
+                    // p 2^jv in fp32 (exp2(-inf) = 0): the row sum adds it in fp32,
+                    // and P' = p 2^jv s_v is rounded to binary16 once
                     float e[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(zs[k][i][j]);   // exp2(-inf) = 0
-                    // p rounded once to fp16; the row sum adds exactly these values
-                    const f16x2_t h0 = {(_Float16)e[0], (_Float16)e[1]}, h1 = {(_Float16)e[2], (_Float16)e[3]};
-                    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-                    l_run[i] = __builtin_amdgcn_fdot2(h0, one2, l_run[i], false);
-                    l_run[i] = __builtin_amdgcn_fdot2(h1, one2, l_run[i], false);
+                    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(zs[k][i][j] + jvf);
+                    l_run[i] += (e[0] + e[1]) + (e[2] + e[3]);
                     u32x2_t packed;
-                    packed[0] = bit_cast<uint32_t>(h0 * vsh[k][0]);
-                    packed[1] = bit_cast<uint32_t>(h1 * vsh[k][1]);
+                    // (the keys' V scales are 0 past the context)
+                    packed[0] = pack_f16x2(e[0] * (float)vsh[k][0][0], e[1] * (float)vsh[k][0][1]);
+                    packed[1] = pack_f16x2(e[2] * (float)vsh[k][1][0], e[3] * (float)vsh[k][1][1]);
                     // reader lane of the 32-row tile t/2: rows 16 (t&1) + li, keys 8 (gq>>1) + 4 (gq&1) + j
                     *reinterpret_cast<u32x2_t*>(pb + ((p * NT32 + (t >> 1)) * 64 + 32 * (gq >> 1) + 16 * (t & 1) + li) * 8 +
                                                 4 * (gq & 1)) = packed;
@@ -557,7 +609,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             // lane (gq, li) holds keys 4 gq + j of the page, row 16 (t0 + i) + li;
             // returns whether a score exceeded its row's threshold
             auto finish_page = [&](int k, const f32x4_t (&acc)[NH], const u32x2_t ks, const u32x2_t vs,
-                                   const bool may_mask, bool& big) -> bool {
+                                   const bool may_mask) -> bool {
                 const int p = 2 * pp + k;
                 float kc[4];
                 kc[0] = f16lo(ks[0]) * zscale;
@@ -578,13 +630,10 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                         vsh[k][j] = bit_cast<f16x2_t>(bit_cast<uint32_t>(vsh[k][j]) & keep);
                     }
                 }
-                // a V scale above 255 leaves no fp16 room above p = 1: slack 0 for the step
+                // a V scale in a higher binade than jv allows flags the step
                 const f16x2_t vm2 = __builtin_elementwise_max(vsh[k][0], vsh[k][1]);
-                vmax2 = __builtin_elementwise_max(vmax2, vm2);
                 const float vmx = fmaxf((float)vm2[0], (float)vm2[1]);
-                const bool bigk = __builtin_amdgcn_ballot_w64(vmx > 255.0f) != 0;
-                big |= bigk;
-                bool exceed = false;
+                bool exceed = vmx >= vlim;
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
 #pragma unroll
@@ -617,12 +666,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                         }
                     }
                     const float mx = fmaxf(fmaxf(zs[k][i][0], zs[k][i][1]), fmaxf(zs[k][i][2], zs[k][i][3]));
-                    exceed |= mx > (bigk ? fminf(thr[i], 0.0f) : thr[i]);
+                    exceed |= mx > (has_ref(i) ? kTau : -INFINITY);
                 }
                 return exceed;
             };
-            auto write_flag = [&](bool exceed, bool big) {
-                const uint32_t flag = (__builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u) | (big ? 2u : 0u);
+            auto write_flag = [&](bool exceed) {
+                const uint32_t flag = __builtin_amdgcn_ballot_w64(exceed) != 0 ? 1u : 0u;
                 if (lane == 0)
                     *reinterpret_cast<uint8_t*>(lds + C::F_OFF + (it & 1) * kWaves + v) = (uint8_t)flag;
             };
@@ -651,17 +700,16 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                     qk_chunk(kraw[0][cc], cc, acc[0]);
                     qk_chunk(kraw[1][cc], cc, acc[1]);
                 }
-                bool big = false;
-                const bool e0 = finish_page(0, acc[0], ks[0], vs[0], false, big);
-                const bool e1 = finish_page(1, acc[1], ks[1], vs[1], false, big);
-                write_flag(e0 || e1, big);
+                const bool e0 = finish_page(0, acc[0], ks[0], vs[0], false);
+                const bool e1 = finish_page(1, acc[1], ks[1], vs[1], false);
+                write_flag(e0 || e1);
             } else {
                 if (do_sm) {
                     softmax_page(0);
                     softmax_page(1);
                 }
                 if (it < n) {
-                    bool exceed = false, big = false;
+                    bool exceed = false;
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
                         if (it <= (k == 0 ? lv0 : lv1)) {
@@ -673,7 +721,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                             for (int i = 0; i < NH; ++i) acc[i] = nqb[i];
 #pragma unroll
                             for (int cc = 0; cc < KB / 2; ++cc) qk_chunk(kraw[cc], cc, acc);
-                            exceed |= finish_page(k, acc, ks, vs, true, big);
+                            exceed |= finish_page(k, acc, ks, vs, true);
                         } else {
 #pragma unroll
                             for (int i = 0; i < NH; ++i) zs[k][i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -692,9 +740,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                             const float mx = group4_max(m4);
                             if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = mx;
                         }
+                        const float vw = wave_max(vscale_max());  // and the V-scale maxima of step 0
+                        if (lane == 0) vxch[v] = vw;
                         exceed = false;
                     }
-                    write_flag(exceed, big);
+                    write_flag(exceed);
                 }
             }
         }
@@ -705,12 +755,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         for (int i = 0; i < NH; ++i) {
             const float l = group4_sum(l_run[i]);
             if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = l;
-            if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = m_ref[i];
+            if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = -nmr[i];   // the reference (any value when l = 0)
         }
-        if (a.out == nullptr) {
-            const float vm = wave_max(fmaxf((float)vmax2[0], (float)vmax2[1]));
-            if (lane == 0) vtop[v] = vm;
-        }
+        if (v == 0 && lane == 0) *jv_out = jv;
         lds_barrier();
         return;
     }
@@ -797,19 +844,13 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
     wait_vmcnt<0>();                                          // the lane-0 copies past the pages
     lds_barrier();                                            // row sums, references, V scale maxima
     if (!owns) return;
-    // ---- epilogue, output side.  fp16 partials are scaled by 2^-k, k from the
-    // largest V scale of the split, so that |o| <= 127 * that scale * 2^-k stays
-    // inside binary16; k goes into the log-sum-exp, which leaves e^lse * o unchanged
-    int kshift = 0;
-    if (a.out == nullptr && a.part_o32 == nullptr) {
-        float vm = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vm = fmaxf(vm, vtop[i]);
-        const float bound = 127.0f * vm;
-        // floor(log2 bound) from the binary32 exponent field (bound is normal here)
-        const int e2 = (int)((bit_cast<uint32_t>(bound) >> 23) & 0xffu) - 127;
-        kshift = bound < 32768.0f ? 0 : max(0, e2 + 1 - 15);
-    }
+    // ---- epilogue, output side.  O and l both carry 2^jv, so O / l is the row
+    // and log2 l is jv above the row's log-sum-exp.  The fp16 partial tiles hold
+    // the rows times 2^jv (at most 127 * 128 in magnitude, whatever V's scale)
+    // with the block's jv beside them for the merge.
+    const int jv = *jv_out;
+    if (a.out == nullptr && a.part_o32 == nullptr && c == 0 && lane == 0)
+        a.part_hjv[((size_t)b * a.Hkv + g) * S + s] = jv;
 #pragma unroll
     for (int r = 0; r < NT32; ++r) {
         const int row = 32 * r + (lane & 31);
@@ -849,7 +890,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 // the wave writes 512 contiguous bytes
                 const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
                 uint16_t* dst = a.part_h + blk * (16 * G * D) + (size_t)(((vs * C::NT32 + r) * 4) * 64 + lane) * 4;
-                const float sc = __builtin_ldexpf(inv, -kshift);
+                const float sc = __builtin_ldexpf(inv, jv);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     u32x2_t x;
@@ -861,12 +902,12 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         }
         if (a.out == nullptr && c == 0 && lane < 32) {
             const float m = rowv[row];
-            const float lse = l > 0.0f ? (m + __builtin_log2f(l) + (float)kshift) * kLn2 : -INFINITY;
+            const float lg = m + __builtin_log2f(l) - (float)jv;
             if (a.part_o32 != nullptr) {
-                a.part_lse32[(((size_t)br * Hq + hq) * a.T_max + t_off + t) * S + s] = lse;
+                a.part_lse32[(((size_t)br * Hq + hq) * a.T_max + t_off + t) * S + s] = l > 0.0f ? lg * kLn2 : -INFINITY;
             } else {
                 const size_t blk = ((size_t)b * a.Hkv + g) * S + s;
-                a.part_hlse[blk * (16 * G) + row] = lse;
+                a.part_hlse[blk * (16 * G) + row] = l > 0.0f ? lg * kLn2 : -INFINITY;
             }
         }
     }
@@ -920,6 +961,7 @@ void verify_partition_kernel(const VerifyArgs a) {
         } else {
             for (int r = threadIdx.x; r < rows; r += kWaves * 64)
                 a.part_hlse[(((size_t)b * a.Hkv + g) * S + s) * (16 * G) + r] = -INFINITY;
+            if (threadIdx.x == 0) a.part_hjv[((size_t)b * a.Hkv + g) * S + s] = 0;
         }
         return;
     }
@@ -947,17 +989,21 @@ struct MergeState {
 
 // One split into the running state (mn finite): an empty split's weight is
 // exp2(-inf) = 0 and its rows, which may hold anything, are zeroed bitwise.
-__device__ __forceinline__ void merge_fold(MergeState& st, float l, u32x2_t x, float mn) {
+// The split's tiles hold its rows times 2^jv: the rows' weight carries 2^-jv,
+// the weight sum does not.
+__device__ __forceinline__ void merge_fold(MergeState& st, float l, int jv, u32x2_t x, float mn) {
     constexpr float kLog2e = 1.4426950408889634f;
-    const float wt = __builtin_amdgcn_exp2f((l - mn) * kLog2e);
+    const float lw = (l - mn) * kLog2e;
+    const float wt = __builtin_amdgcn_exp2f(lw);
+    const float wo = __builtin_amdgcn_exp2f(lw - (float)jv);
     const uint32_t keep = l != -INFINITY ? 0xffffffffu : 0u;
     x[0] &= keep;
     x[1] &= keep;
     st.W += wt;
-    st.acc[0] = __builtin_fmaf(wt, f16lo(x[0]), st.acc[0]);
-    st.acc[1] = __builtin_fmaf(wt, f16hi(x[0]), st.acc[1]);
-    st.acc[2] = __builtin_fmaf(wt, f16lo(x[1]), st.acc[2]);
-    st.acc[3] = __builtin_fmaf(wt, f16hi(x[1]), st.acc[3]);
+    st.acc[0] = __builtin_fmaf(wo, f16lo(x[0]), st.acc[0]);
+    st.acc[1] = __builtin_fmaf(wo, f16hi(x[0]), st.acc[1]);
+    st.acc[2] = __builtin_fmaf(wo, f16lo(x[1]), st.acc[2]);
+    st.acc[3] = __builtin_fmaf(wo, f16hi(x[1]), st.acc[3]);
 }
 
 __device__ __forceinline__ void merge_rescale(MergeState& st, float mn) {
@@ -993,11 +1039,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
     const size_t blk0 = ((size_t)b * a.Hkv + g) * S;
     const uint16_t* src = a.part_h + blk0 * (ROWS * D) + (size_t)(((v * NT32 + r) * 4 + q4) * 64 + lane) * 4;
     const float* lse = a.part_hlse + blk0 * ROWS + row;
+    const int* jvs = a.part_hjv + blk0;
 
     MergeState st{-INFINITY, 0.0f, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     for (int s0 = s_begin; s0 < s_end; s0 += kMergeBatch) {
         u32x2_t x[kMergeBatch];
         float l[kMergeBatch];
+        int jw[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             // every load is issued (a split past the range re-reads the last
@@ -1005,6 +1053,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
             const uint32_t sp = (uint32_t)min(s0 + u, s_end - 1);
             x[u] = *reinterpret_cast<const u32x2_t*>(src + sp * (uint32_t)(ROWS * D));
             l[u] = lse[sp * (uint32_t)ROWS];
+            jw[u] = jvs[sp];
         }
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) l[u] = s0 + u < s_end ? l[u] : -INFINITY;
@@ -1016,7 +1065,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void splitk_merge_tiled_kernel(co
         merge_rescale(st, mn);
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u)
-            merge_fold(st, l[u], x[u], mn);
+            merge_fold(st, l[u], jw[u], x[u], mn);
     }
     if constexpr (!ALL_SPLITS) {
         if (wv > 0) {

@@ -113,7 +113,7 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
                   D: int, num_pages: int, P: int = 16, draft_lens=None, values: str = "quantized",
                   placement: str = "random", shared_prefix: int = 0, nan_pad_q: bool = False,
                   sm_scale: float | None = None, extra_pages: int = 0, k_mag: float = 1.0,
-                  v_mag: float = 1.0, k_spike=None) -> Workload:
+                  v_mag: float = 1.0, k_spike=None, v_gain=None) -> Workload:
     """Build one seeded workload.
 
     values: "quantized" -> fp32 N(0,1) K/V source rows appended through the
@@ -129,6 +129,9 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
     vector per kv head (drawn last, after the draft lengths).  Rising amplitudes
     put a row's largest score late in the context ("quantized" values, no
     shared prefix).
+    v_gain: None, or a function gain(pos, ctx) -> float array multiplying the V
+    source row at each context position of a request (V scales that grow or
+    shrink along the context; "quantized" values, no shared prefix).
     shared_prefix: tokens (a whole number of pages) that every request shares
     through identical block-table entries.
     """
@@ -202,6 +205,12 @@ def make_workload(name: str, seed: int, *, B: int, context_lens, T_max: int, Hq:
             start = sum(own[:b])
             amp = np.asarray(k_spike(np.arange(own[b]), int(ctx[b])), dtype=np.float32)
             k_all[start:start + own[b]] += amp[:, None, None] * w[None]
+    if v_gain is not None:
+        assert values == "quantized" and shared_prefix == 0, "V gains take private quantised contexts"
+        for b in range(B):
+            start = sum(own[:b])
+            gain = np.asarray(v_gain(np.arange(own[b]), int(ctx[b])), dtype=np.float32)
+            v_all[start:start + own[b]] *= gain[:, None, None]
 
     if nan_pad_q:
         for b in range(B):

@@ -19,11 +19,16 @@ BF16_NAN = 0x7FC0
 # |o| >= 2.56)
 REL_L2 = 2e-3
 ABS = 1e-2
-# per element, beside the above: |got - ref| <= half an ulp of bf16(ref) + MAG_REL * mag, where
-# mag = sum_j w_j |v_j| / sum_j w_j is the attention of |V| (the size of the row before the
-# signs of V cancel).  The kernel rounds p, P' = p s_v and split partials to fp16, each a
-# relative 2^-11 of that size; 2^-8 leaves a margin of 2 over their sum.
+# per element, beside the above: |got - ref| <= half an ulp of bf16(ref) + MAG_REL * mag + floor,
+# where mag = sum_j w_j |v_j| / sum_j w_j is the attention of |V| (the size of the row before
+# the signs of V cancel).  The kernel rounds P' = p 2^jv s_v and the split partials to fp16,
+# each a relative 2^-11 of that size; 2^-8 leaves a margin of 2 over their sum.  A P' below
+# binary16's normal range is rounded to an absolute 2^-25 instead: in output units at most
+# 2^-25 * 127 / 2^jv per key, with 2^jv >= 64 / s_max and the row sum >= 1, i.e. under
+# 2^-24 N s_max over N visible keys (s_max the request's largest V scale); the floor takes
+# 2^-23 N s_max.
 MAG_REL = 2.0 ** -8
+FLOOR_REL = 2.0 ** -23
 
 
 def log(msg):
@@ -55,11 +60,13 @@ def half_ulp_bf16(ref):
     return np.where(a > 0, 2.0 ** (e - 8), 0.0)
 
 
-def attn_error(got, ref):
-    """got, ref: fp64 arrays of the same shape (valid rows only)."""
+def attn_error(got, ref, v_scale=1.0):
+    """got, ref: fp64 arrays of the same shape (valid rows only).  v_scale: the
+    magnitude V was drawn at (attention is linear in V, so the absolute slack
+    of 1e-2, stated for unit-scale V, scales with it)."""
     diff = got - ref
     rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
-    bound = ABS + half_ulp_bf16(ref)
+    bound = ABS * v_scale + half_ulp_bf16(ref)
     excess = float(np.max(np.abs(diff) - bound)) if diff.size else -1.0
     ref_bf16 = bf16_to_f64(_round_bf16(ref))
     ulps = float(np.max(np.abs(got - ref_bf16) / np.maximum(2 * half_ulp_bf16(ref), 1e-300))) if diff.size else 0.0
@@ -73,16 +80,19 @@ def _round_bf16(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
 
 
-def assert_attn_ok(got, ref, where, mag=None):
-    """mag: the attention of |V| for the same rows (enables the per-element bound)."""
-    e = attn_error(got, ref)
+def assert_attn_ok(got, ref, where, mag=None, v_scale=1.0, floor=None):
+    """mag: the attention of |V| for the same rows (enables the per-element bound);
+    floor: per row, the binary16 underflow term of that bound (0 if None);
+    v_scale: the magnitude V was drawn at (scales the absolute slack)."""
+    e = attn_error(got, ref, v_scale)
     log(f"  {where}: rel_l2={e['rel_l2']:.3e} max|err|={e['max_abs']:.3e} "
         f"bound_excess={e['bound_excess']:.2e} ulps_vs_bf16(ref)={e['max_ulps_vs_bf16_ref']:.2f}")
     assert e["finite"], f"{where}: non-finite output"
     assert e["rel_l2"] <= REL_L2, f"{where}: relative L2 {e['rel_l2']:.3e}"
-    assert e["bound_excess"] <= 0, f"{where}: an element exceeds 1e-2 + half a bf16 ulp"
+    assert e["bound_excess"] <= 0, f"{where}: an element exceeds {ABS * v_scale:.0e} + half a bf16 ulp"
     if mag is not None:
-        ratio = (np.abs(got - ref) - half_ulp_bf16(ref)) / np.maximum(mag, 1e-300)
+        fl = 0.0 if floor is None else np.asarray(floor, np.float64).reshape(-1, *([1] * (got.ndim - 1)))
+        ratio = (np.abs(got - ref) - half_ulp_bf16(ref) - fl) / np.maximum(mag, 1e-300)
         worst = float(ratio.max()) if ratio.size else 0.0
         log(f"    per element: max (|err| - half ulp) / mag = {worst:.2e} (bound {MAG_REL:.2e})")
         assert worst <= MAG_REL, f"{where}: an element exceeds half a bf16 ulp + {MAG_REL:.2e} * mag"
@@ -144,6 +154,21 @@ class Prepared:
             kp, vp, ks, vs = self.pools
             self._abs_pools = [kp, np.abs(vp.astype(np.int16)).astype(np.int8), ks, vs]
         return self._abs_pools
+
+    def p_floor(self, rows):
+        """Per row (b, t, h): FLOOR_REL * (keys the row sees) * (request b's largest V scale)."""
+        wl = self.wl
+        if not hasattr(self, "_smax"):
+            vs = self.pools[3].view(np.float16).astype(np.float64)
+            self._smax = np.zeros(wl.B)
+            for b in range(wl.B):
+                pos = np.arange(int(wl.context_lens[b]))
+                if pos.size:
+                    self._smax[b] = vs[wl.block_table[b, pos // wl.P], :, pos % wl.P].max()
+        rows = np.asarray(rows)
+        b, t = rows[:, 0], rows[:, 1]
+        n = wl.context_lens[b].astype(np.float64) - wl.draft_lens[b] + t + 1
+        return FLOOR_REL * n * self._smax[b]
 
     def oracle_rows(self, rows, abs_v=False):
         wl = self.wl

@@ -42,10 +42,11 @@ def test_status_strings(lib):
 
 def test_workspace_and_split_arithmetic(lib):
     # tiled fp16 partials for 16 drafts of every query head per split, then
-    # 256-aligned fp32 log-sum-exps (T_max does not change the size)
+    # 256-aligned fp32 log-sum-exps, then an int32 exponent per (request, head,
+    # split) block (T_max does not change the size)
     assert sda.splash_verify_attn_workspace_bytes(1, 16, 24, 256, 1) == 0
     rows = 1 * 16 * 24 * 64
-    want = -(-rows * 256 * 2 // 256) * 256 + -(-rows * 4 // 256) * 256
+    want = -(-rows * 256 * 2 // 256) * 256 + -(-rows * 4 // 256) * 256 + -(-24 * 64 * 4 // 256) * 256
     assert sda.splash_verify_attn_workspace_bytes(1, 3, 24, 256, 64) == want
     assert sda.splash_verify_attn_workspace_bytes(1, 16, 24, 256, 64) == want
     # pages per split are whole steps of 4 pages

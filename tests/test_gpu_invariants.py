@@ -33,7 +33,7 @@ def check_full(prep, out, where):
     if len(rows) == 0:
         return
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, prep.oracle_rows(rows), where, mag=prep.oracle_rows(rows, abs_v=True))
+    assert_attn_ok(got, prep.oracle_rows(rows), where, mag=prep.oracle_rows(rows, abs_v=True), floor=prep.p_floor(rows))
     for b in range(wl.B):
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN), f"{where}: row written"
 

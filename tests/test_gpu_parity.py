@@ -40,7 +40,7 @@ def test_verify_matches_oracle(cfg):
     rows = prep.valid_rows()                                # every row of every request
     ref = prep.oracle_rows(rows)
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, ref, f"config {cfg} ({len(rows)} rows)", mag=prep.oracle_rows(rows, abs_v=True))
+    assert_attn_ok(got, ref, f"config {cfg} ({len(rows)} rows)", mag=prep.oracle_rows(rows, abs_v=True), floor=prep.p_floor(rows))
     # rows past each request's draft are never written
     for b in range(wl.B):
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
@@ -53,7 +53,7 @@ def test_split_count_sweep(S):
     rows = prep.valid_rows()
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
     ref = prep.oracle_rows(rows)
-    assert_attn_ok(got, ref, f"config 2, {S} splits", mag=prep.oracle_rows(rows, abs_v=True))
+    assert_attn_ok(got, ref, f"config 2, {S} splits", mag=prep.oracle_rows(rows, abs_v=True), floor=prep.p_floor(rows))
 
 
 def split_reference(prep, S):
@@ -81,7 +81,7 @@ def run_partition(prep, S):
     return part_o, part_lse
 
 
-@pytest.mark.parametrize("v_mag", [1.0, 3e4])
+@pytest.mark.parametrize("v_mag", [1.0, 3e4, 1e-4])
 def test_partition_partials_match_oracle_split(v_mag):
     """fp32 partial rows and log-sum-exps of each split, element by element,
     including empty splits (lse -inf, zero row); then the exported merge of
@@ -106,7 +106,10 @@ def test_partition_partials_match_oracle_split(v_mag):
         assert err_l.max() <= 1e-3, f"lse error {err_l.max():.2e}"
         r_o, g_o, m_o = ro[b, :, :d][live], go[b, :, :d][live], mo[b, :, :d][live]
         assert np.all(np.isfinite(g_o))
-        ratio = np.abs(g_o - r_o) / np.maximum(m_o, 1e-300)
+        # the binary16 underflow floor of each row, over its split's keys at most
+        fl = prep.p_floor(np.array([(b, t, 0) for t in range(d)]))            # [d]
+        fl = np.broadcast_to(fl[None, :, None], live.shape)[live][:, None]
+        ratio = (np.abs(g_o - r_o) - fl) / np.maximum(m_o, 1e-300)
         worst_o, worst_l = max(worst_o, float(ratio.max())), max(worst_l, float(err_l.max()))
         assert ratio.max() <= MAG_REL, f"request {b}: partial element off by {ratio.max():.2e} of its size"
     log(f"  partials (v_mag {v_mag}): max |err| / mag {worst_o:.2e}, max |d lse| {worst_l:.2e}")
@@ -117,7 +120,7 @@ def test_partition_partials_match_oracle_split(v_mag):
     rows = prep.valid_rows()
     got = bf16_to_f64(out.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]])
     assert_attn_ok(got, prep.oracle_rows(rows), f"partition + merge (v_mag {v_mag})",
-                   mag=prep.oracle_rows(rows, abs_v=True))
+                   mag=prep.oracle_rows(rows, abs_v=True), floor=prep.p_floor(rows), v_scale=v_mag)
 
 
 @pytest.mark.parametrize("shape", [(24, 256), (16, 128), (8, 64)])

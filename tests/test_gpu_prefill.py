@@ -32,7 +32,7 @@ def check_prefill(prep, num_splits, where):
     rows = prep.valid_rows()
     ref = prep.oracle_rows(rows)
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
-    assert_attn_ok(got, ref, where, mag=prep.oracle_rows(rows, abs_v=True))
+    assert_attn_ok(got, ref, where, mag=prep.oracle_rows(rows, abs_v=True), floor=prep.p_floor(rows))
     for b in range(wl.B):                                     # rows past each chunk stay untouched
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
 

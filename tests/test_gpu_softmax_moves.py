@@ -126,7 +126,7 @@ def test_reference_moves_match_oracle(name, S):
     rows = prep.valid_rows()
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
     assert_attn_ok(got, prep.oracle_rows(rows), f"{name}, {S or 'preset'} splits",
-                   mag=prep.oracle_rows(rows, abs_v=True))
+                   mag=prep.oracle_rows(rows, abs_v=True), floor=prep.p_floor(rows), v_scale=WORKLOADS[name].get("v_mag", 1.0))
     for b in range(wl.B):
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
 

@@ -36,7 +36,8 @@ def check_tree(prep, masks, num_splits, where):
     got = bf16_to_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]])
     mag = oracle.load().verify_attn_masked(wl.q, *prep.abs_pools, wl.block_table, wl.context_lens, wl.draft_lens,
                                            wl.Hkv, wl.sm_scale, masks)
-    assert_attn_ok(got, ref[rows[:, 0], rows[:, 1], rows[:, 2]], where, mag=mag[rows[:, 0], rows[:, 1], rows[:, 2]])
+    assert_attn_ok(got, ref[rows[:, 0], rows[:, 1], rows[:, 2]], where, mag=mag[rows[:, 0], rows[:, 1], rows[:, 2]],
+                   floor=prep.p_floor(rows))
     for b in range(wl.B):                                     # rows past the draft stay untouched
         assert np.all(out[b, int(wl.draft_lens[b]):].view(np.uint16) == BF16_NAN)
 
