@@ -168,6 +168,33 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * splash_verify_attn_noalloc -- splash_verify_attn for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument; the split partials go to a scratch
+ * array the library holds in device memory, SPLASH_NOALLOC_SCRATCH_BYTES bytes
+ * on each GPU it runs on, kept until the process ends.  The call allocates
+ * nothing.  A call whose splits need more than that
+ * (splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S) for the S it runs,
+ * the preset when num_splits = 0) returns SPLASH_ERR_WORKSPACE_TOO_SMALL before
+ * anything is launched, and SPLASH_ERR_DEVICE if the scratch's address cannot
+ * be found.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (different streams without ordering between
+ * them) race and give undefined results; calls on one stream do not.  The
+ * scratch holds only partials each call writes before reading, so nothing in
+ * it needs clearing.  Arguments, results and errors otherwise as
+ * splash_verify_attn (same kernels: for the same num_splits the output is
+ * bit-identical).
+ */
+#define SPLASH_NOALLOC_SCRATCH_BYTES (32u << 20)
+int splash_verify_attn_noalloc(const uint16_t* q, uint16_t* out,
+                               const int8_t* k_pool, const int8_t* v_pool,
+                               const uint16_t* k_scale, const uint16_t* v_scale,
+                               const int32_t* block_table, int max_pages_per_seq,
+                               const int32_t* context_lens, const int32_t* draft_lens,
+                               int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                               int max_context_len, float sm_scale, int num_splits, void* stream);
+
+/*
  * splash_verify_attn_masked -- splash_verify_attn with a tree-shaped mask
  * inside the block instead of the causal chain.  DFlash 2's path selector picks
  * a coherent path among several candidate tokens per position (discuss.pytorch.kr

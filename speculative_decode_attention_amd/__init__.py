@@ -32,6 +32,7 @@ EXPORTED = (
     "splash_verify_attn_default_splits",
     "splash_verify_attn_workspace_bytes",
     "splash_verify_attn",
+    "splash_verify_attn_noalloc",
     "splash_verify_attn_masked",
     "splash_verify_attn_window",
     "splash_verify_attn_window_tokens",
@@ -74,6 +75,8 @@ def load_library(path: Path | None = None):
     lib.splash_verify_attn_workspace_bytes.restype = _Z
     lib.splash_verify_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_verify_attn_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                               _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]
     lib.splash_verify_attn_masked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                                               _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
     lib.splash_verify_attn_window.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I,
@@ -231,6 +234,32 @@ def splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, co
     """
     return _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
                    max_context_len, sm_scale, num_splits, workspace, stream, None)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20                    # SPLASH_NOALLOC_SCRATCH_BYTES
+
+
+def splash_verify_attn_noalloc(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
+                               max_context_len, sm_scale, num_splits=0, stream=None):
+    """splash_verify_attn with the split partials in the library's own device
+    scratch (no workspace, nothing allocated); calls overlapping on one GPU race."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B][T_max][Hq][D]")
+    B, T_max, Hq, Dq = q.shape
+    _dev(q, "q", (torch.bfloat16, torch.int16))
+    _dev(out, "out", (torch.bfloat16, torch.int16), tuple(q.shape))
+    num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
+    if Dq != D:
+        raise ValueError("q head dim does not match the pools")
+    maxp = _lens(block_table, context_lens, draft_lens, B)
+    rc = _lib().splash_verify_attn_noalloc(
+        q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_scale.data_ptr(),
+        v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(), draft_lens.data_ptr(),
+        B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len), float(sm_scale), int(num_splits),
+        _stream(stream))
+    _check(rc, "splash_verify_attn_noalloc")
+    return out
 
 
 def splash_verify_attn_masked(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,

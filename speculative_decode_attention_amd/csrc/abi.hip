@@ -13,6 +13,9 @@
 
 using namespace splash;
 
+// file scope, one copy per device, held until the process ends
+static __device__ __align__(256) uint8_t scratch[SPLASH_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -26,6 +29,13 @@ constexpr int kMinPagesPerSplit = 8;
 std::mutex g_cu_mutex;
 int g_cu_count[kMaxDevices] = {0};
 
+// Split-partial scratch of splash_verify_attn_noalloc (its largest size is
+// SPLASH_NOALLOC_SCRATCH_BYTES).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)SPLASH_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
 int device_cu_count() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
@@ -38,6 +48,19 @@ int device_cu_count() {
         g_cu_count[dev] = cus;
     }
     return g_cu_count[dev];
+}
+
+// The current device's address of `scratch` (nullptr if the query fails).
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -198,6 +221,33 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
                             sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int splash_verify_attn_noalloc(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
+                               const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                               int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
+                               int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                               int max_context_len, float sm_scale, int num_splits, void* stream) {
+    int rc = check_verify_common(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
+                                 max_pages_per_seq, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len, sm_scale);
+    if (rc != SPLASH_OK) return rc;
+    if (!out || !aligned16(out) || num_splits < 0) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (B == 0 || T_max == 0 || max_context_len == 0) return SPLASH_OK;
+    // the split count the call will use, and so the partials it needs
+    int S = num_splits;
+    if (S == 0) {
+        S = splash_verify_attn_default_splits(B, Hkv, max_context_len, P, D);
+        if (S < 0) return -S;
+    }
+    const int L = pages_per_split(max_context_len, P, S);
+    S = ceil_div(ceil_div(max_context_len, P), L);
+    const size_t need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S);
+    if (need > kScratchBytes) return SPLASH_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (need > 0 && (ws = scratch_address()) == nullptr) return SPLASH_ERR_DEVICE;
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
+                            sm_scale, S, ws, need > 0 ? kScratchBytes : 0, stream, nullptr, 0);
 }
 
 int splash_verify_attn_masked(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
