@@ -186,6 +186,16 @@ __device__ __forceinline__ uint32_t pack_f16x2(float x, float y) {
     return bit_cast<uint32_t>(h);
 }
 
+// (x * s.lo, y * s.hi) as a packed binary16 pair: an fp32 weight times a
+// binary16 scale, each product rounded to binary16 (two mixed-precision FMAs
+// with a zero addend; register operands only).
+__device__ __forceinline__ uint32_t mul_f32_f16x2(float x, float y, uint32_t s) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(s));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(y), "v"(s));
+    return r;
+}
+
 // Shapes and the LDS arena of one workgroup.
 template <int D, int G>
 struct Cfg {
@@ -425,7 +435,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 for (int i = 0; i < NH; ++i) nqb[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qf[kb][i], nqb[i], 0, 0, 0);
         }
         // per-row state of this half's tiles (row 16 (t0 + i) + li, the same in all lanes of a row)
-        // nmr = minus the row's reference (0 until it has one).  hasref: bit
+        // nmr = jv minus the row's reference m (the reference is 0 until the row
+        // has one), so that scores come out as z - m + jv and exp2 of them is the
+        // weight p 2^jv the softmax carries.  hasref: bit
         // 16 i + li is set once row 16 (t0 + i) + li has a reference (a scalar
         // mask: every lane of a row agrees on it, and it costs no VGPR)
         float nmr[NH], l_run[NH];
@@ -505,8 +517,10 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 }
                 lds_barrier();
                 // the O factor of a V-exponent change is an exact power of two (a
-                // rise of jv only happens while every scale seen was 0, so O = 0)
-                float vscale = 1.0f;
+                // rise of jv only happens while every scale seen was 0, so O = 0);
+                // the scores held carry the old jv
+                float vscale = 1.0f, dj = 0.0f;
+                const float jv_old = jvf;
                 {
                     const float vnew = bit_cast<float>(__builtin_amdgcn_readfirstlane(
                         bit_cast<uint32_t>(fmaxf(fmaxf(vxch[0], vxch[1]), fmaxf(vxch[2], vxch[3])))));
@@ -514,12 +528,14 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                         const int old = jv;
                         set_jv(fmaxf(vrun, vnew));
                         vscale = __builtin_ldexpf(1.0f, jv - old);
+                        dj = (float)(jv - old);
                     }
                 }
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const u32x2_t mw = *reinterpret_cast<const u32x2_t*>(red + (16 * (t0 + i) + li) * 2);
-                    const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));
+                    // the step's maximum above the row's reference
+                    const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1])) - jv_old;
                     const bool fresh = !has_ref(i);
                     const bool move = fresh ? mstep > -INFINITY : mstep > kTau;
                     float alpha = 1.0f;
@@ -532,6 +548,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 #pragma unroll
                             for (int j = 0; j < 4; ++j) zs[k][i][j] -= mstep;
                     }
+                    nmr[i] += dj;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) zs[k][i][j] += dj;
                     l_run[i] *= vscale;
                     if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = alpha * vscale;
                     hasref |= (__builtin_amdgcn_ballot_w64(move) & 0xffffull) << (16 * i);   // lanes gq = 0
@@ -547,10 +568,15 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 #pragma unroll
                 for (int i = 0; i < NH; ++i) {
                     const u32x2_t mw = *reinterpret_cast<const u32x2_t*>(red + (16 * (t0 + i) + li) * 2);
-                    const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));
+                    const float mstep = fmaxf(bit_cast<float>(mw[0]), bit_cast<float>(mw[1]));   // step 0 scored with jv = 0
                     hasref |= (__builtin_amdgcn_ballot_w64(mstep > -INFINITY) & 0xffffull) << (16 * i);
+                    nmr[i] = jvf;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) zs[k][i][j] += jvf;
                     if (mstep > -INFINITY) {
-                        nmr[i] = -mstep;
+                        nmr[i] = jvf - mstep;
 #pragma unroll
                         for (int k = 0; k < 2; ++k)
 #pragma unroll
@@ -569,15 +595,15 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                 for (int i = 0; i < NH; ++i) {
                     const int t = t0 + i;
                     // p 2^jv in fp32 (exp2(-inf) = 0): the row sum adds it in fp32,
-                    // and P' = p 2^jv s_v is rounded to binary16 once
+                    // and P' = p 2^jv s_v is rounded to binary16 once (the keys' V
+                    // scales are 0 past the context)
                     float e[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(zs[k][i][j] + jvf);
+                    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(zs[k][i][j]);
                     l_run[i] += (e[0] + e[1]) + (e[2] + e[3]);
                     u32x2_t packed;
-                    // (the keys' V scales are 0 past the context)
-                    packed[0] = pack_f16x2(e[0] * (float)vsh[k][0][0], e[1] * (float)vsh[k][0][1]);
-                    packed[1] = pack_f16x2(e[2] * (float)vsh[k][1][0], e[3] * (float)vsh[k][1][1]);
+                    packed[0] = mul_f32_f16x2(e[0], e[1], bit_cast<uint32_t>(vsh[k][0]));
+                    packed[1] = mul_f32_f16x2(e[2], e[3], bit_cast<uint32_t>(vsh[k][1]));
                     // reader lane of the 32-row tile t/2: rows 16 (t&1) + li, keys 8 (gq>>1) + 4 (gq&1) + j
                     *reinterpret_cast<u32x2_t*>(pb + ((p * NT32 + (t >> 1)) * 64 + 32 * (gq >> 1) + 16 * (t & 1) + li) * 8 +
                                                 4 * (gq & 1)) = packed;
@@ -611,6 +637,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             auto finish_page = [&](int k, const f32x4_t (&acc)[NH], const u32x2_t ks, const u32x2_t vs,
                                    const bool may_mask) -> bool {
                 const int p = 2 * pp + k;
+                const float thr_ref = kTau + jvf;             // a row with a reference: its slack above m - jv
                 float kc[4];
                 kc[0] = f16lo(ks[0]) * zscale;
                 kc[1] = f16hi(ks[0]) * zscale;
@@ -666,7 +693,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                         }
                     }
                     const float mx = fmaxf(fmaxf(zs[k][i][0], zs[k][i][1]), fmaxf(zs[k][i][2], zs[k][i][3]));
-                    exceed |= mx > (has_ref(i) ? kTau : -INFINITY);
+                    exceed |= mx > (has_ref(i) ? thr_ref : -INFINITY);
                 }
                 return exceed;
             };
@@ -755,7 +782,7 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         for (int i = 0; i < NH; ++i) {
             const float l = group4_sum(l_run[i]);
             if (gq == 0) red[(16 * (t0 + i) + li) * 2 + pp] = l;
-            if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = -nmr[i];   // the reference (any value when l = 0)
+            if (pp == 0 && gq == 0) rowv[16 * (t0 + i) + li] = jvf - nmr[i];   // the reference (any value when l = 0)
         }
         if (v == 0 && lane == 0) *jv_out = jv;
         lds_barrier();
@@ -773,23 +800,34 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             for (int e = 0; e < 16; ++e) o[sl][r][e] = 0.0f;
     int id_k = clamp_page(idj[kKAhead]);                      // K page of the next copies
     int id_v = clamp_page(idj[1]);                            // V page of the next copies
+    // From iteration last_c on, every copy this wave would issue (K(it + 3),
+    // V(it + 1), the page id of step it + 7) is past the split's pages of
+    // column c: from iteration E on the wave issues none (positions before 2
+    // keep the start-up's fixed counts), and the tail's waits count what
+    // actually went out, so no copy is left to wait for after the loop.
+    const int E = max(2, last_c);
 
     for (int it = 0; it < n + 2; ++it) {
         // this wave's copies of K(it) and V(it - 2) (position it - 3) have
         // landed: at most the copies of positions it - 2 and it - 1 are in flight
-        if (it >= 2) wait_vmcnt<2 * (KC_STEP + NI)>();
-        else if (it == 1) wait_vmcnt<KC_START + KC_STEP + 2 * NI>();
+        if (it >= 2) {
+            if (it - 1 < E) wait_vmcnt<2 * (KC_STEP + NI)>();
+            else if (it - 2 < E) wait_vmcnt<KC_STEP + NI>();
+            else wait_vmcnt<0>();
+        } else if (it == 1) wait_vmcnt<KC_START + KC_STEP + 2 * NI>();
         else wait_vmcnt<2 * KC_START + NI>();
         lds_barrier();
         const bool do_sm = it >= 1 && it <= n;
         const uint32_t flags = do_sm ? read_flags(it - 1) : 0u;
         // ---- copies for later steps; a page id past the split's pages is read
         // from the split's first entry of page c's column, which always exists
-        issue_k(it + kKAhead, id_k);
-        issue_v(it + 1, id_v);
-        if (lane == 0)
-            dma4_to_lds(it + kIdAhead <= last_c ? bt + 4 * (it + kIdAhead) : bt - c,
-                        lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + c) * 4);
+        if (it < E) {
+            issue_k(it + kKAhead, id_k);
+            issue_v(it + 1, id_v);
+            if (lane == 0)
+                dma4_to_lds(it + kIdAhead <= last_c ? bt + 4 * (it + kIdAhead) : bt - c,
+                            lds_base + C::ID_OFF + (((it + kIdAhead) & (kIdRing - 1)) * kPagesPerIter + c) * 4);
+        }
 
         // ---- P V of step it - 2: O^T += V^T P'^T for this wave's columns.
         // Every operand is read first, so the LDS round trips overlap.
