@@ -8,7 +8,10 @@ discuss.pytorch.kr, section "benchmark method").
 
 One step = the whole hot path on one batch: append the drafted block's K/V
 (quantise to int8 into the paged pools) and run block-verify attention over the
-full context.  Inputs are resident in HBM before timing.  Steps rotate over R
+full context, as one call (splash_verify_attn_append: the workgroups holding
+the block's pages quantise it, attend to it and store it).  The same work as
+two calls, the append and then the verify call, is reported beside it.
+Inputs are resident in HBM before timing.  Steps rotate over R
 disjoint replicas of the request's pages (identical values, R * 68 MB >= 1 GiB)
 so that the 256 MB Infinity Cache cannot serve the context from one step to
 the next.
@@ -307,9 +310,14 @@ def main():
     def verify(r):
         sda.splash_verify_attn(q, out, *pools, bts[r], ctx_t, dl_t, ctx, wl.sm_scale, num_splits=S_req, workspace=ws)
 
-    def step(r):
+    def step_seq(r):
         sda.splash_kv_append_int8(k_new, v_new, *pools, bts[r], ctx_t, dl_t)
         verify(r)
+
+    # the step as one launch: the verify call appends the block itself
+    def step(r):
+        sda.splash_verify_attn_append(k_new, v_new, q, out, *pools, bts[r], ctx_t, dl_t, ctx, wl.sm_scale,
+                                      num_splits=S_req, workspace=ws)
 
     # the same call with a tree-shaped block mask (random candidate tree)
     tree = torch.from_numpy(synth.tree_block_masks(77, wl.draft_lens, T).view(np.int32)).to(dev)
@@ -327,13 +335,14 @@ def main():
     cap = torch.cuda.Stream()
     # eager calls first (every lazy init done), then the graphs
     for r in range(R):
+        step_seq(r)
         step(r)
     verify_tree(0)
     verify_window(0)
     torch.cuda.synchronize()
     PHASES.add("eager warm-up, 32K", R)
     rot = {name: Rotation([(lambda r=r, f=fn: f(r)) for r in range(R)], args.steps, cap)
-           for name, fn in (("verify", verify), ("step", step), ("verify_tree", verify_tree),
+           for name, fn in (("verify", verify), ("step", step), ("step_seq", step_seq), ("verify_tree", verify_tree),
                             ("verify_window", verify_window))}
     torch.cuda.synchronize()
 
@@ -341,7 +350,8 @@ def main():
     us_verify, per_verify = rot["verify"].time(args.steps, args.warmup)
     PHASES.add("verify call, 32K, rotating replicas (roofline)", rot["verify"].calls)
     us_step, per_step = rot["step"].time(args.steps, args.warmup)
-    PHASES.add("append + verify steps, 32K", rot["step"].calls)
+    us_step_seq, _ = rot["step_seq"].time(args.steps, args.warmup)
+    PHASES.add("append + verify steps, 32K", rot["step_seq"].calls)
     us_tree, _ = rot["verify_tree"].time(args.steps, args.warmup)
     us_window, _ = rot["verify_window"].time(args.steps, args.warmup)
     ms_step = us_step * 1e-3
@@ -399,6 +409,8 @@ def main():
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_tokens": P, "kv_dtype": "int8", "io_dtype": "bf16",
                    "splits": S, "replicas": R, "rotated_bytes": R * call_bytes, "step_bytes": step_bytes,
                    "batches": BATCHES, "step_us_batches": [round(x, 2) for x in per_step],
+                   "step": "splash_verify_attn_append: the block appended and verified in one call",
+                   "step_sequential_us": round(us_step_seq, 2),
                    "verify_us_per_call": round(us_verify, 2),
                    "verify_us_batches": [round(x, 2) for x in per_verify],
                    "verify_gbs": round(achieved, 1),

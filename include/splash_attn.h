@@ -168,6 +168,37 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * splash_verify_attn_append -- the step that appends the drafted block to the
+ * cache and verifies it, as one call: splash_kv_append_int8 and
+ * splash_verify_attn fused (a decode step goes to the GPU as one unit:
+ * discuss.pytorch.kr summary, section "DFlash 2 speculative decoding as the
+ * default path").  k_new / v_new are the block's source rows, [B][T_max][Hkv][D]
+ * in fp32 or bf16 as src_dtype (the arguments splash_kv_append_int8 takes);
+ * block token t < draft_lens[b] sits at position context_lens[b] - draft_lens[b]
+ * + t, whose page must be in block_table.  The workgroups whose split holds the
+ * block's pages quantise its rows exactly as the append does and store them
+ * into the pools' slots of those pages before they copy the pages (a split
+ * of fewer than 24 pages holding the block starts its copies later for
+ * that).  On return (stream order) the pools are byte-identical to those
+ * splash_kv_append_int8 leaves, and out is bit-identical to splash_verify_attn's
+ * after it with the same num_splits.  A block page id outside [0, num_pages)
+ * is not written.  The pools are written, so nothing else may read or write
+ * the block's pages during the call.
+ * Errors as splash_verify_attn, plus SPLASH_ERR_INVALID_ARGUMENT for a null
+ * k_new / v_new, an unknown src_dtype, or source rows not aligned to D / 64
+ * elements.
+ */
+int splash_verify_attn_append(const void* k_new, const void* v_new, int src_dtype,
+                              const uint16_t* q, uint16_t* out,
+                              int8_t* k_pool, int8_t* v_pool,
+                              uint16_t* k_scale, uint16_t* v_scale,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* context_lens, const int32_t* draft_lens,
+                              int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
+                              int max_context_len, float sm_scale, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * splash_verify_attn_noalloc -- splash_verify_attn for callers that cannot
  * allocate (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): no workspace argument; the split partials go to a scratch

@@ -32,6 +32,7 @@ EXPORTED = (
     "splash_verify_attn_default_splits",
     "splash_verify_attn_workspace_bytes",
     "splash_verify_attn",
+    "splash_verify_attn_append",
     "splash_verify_attn_noalloc",
     "splash_verify_attn_masked",
     "splash_verify_attn_window",
@@ -75,6 +76,8 @@ def load_library(path: Path | None = None):
     lib.splash_verify_attn_workspace_bytes.restype = _Z
     lib.splash_verify_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+    lib.splash_verify_attn_append.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                              _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
     lib.splash_verify_attn_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                                _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]
     lib.splash_verify_attn_masked.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,
@@ -234,6 +237,44 @@ def splash_verify_attn(q, out, k_pool, v_pool, k_scale, v_scale, block_table, co
     """
     return _verify(q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, draft_lens,
                    max_context_len, sm_scale, num_splits, workspace, stream, None)
+
+
+def splash_verify_attn_append(k_new, v_new, q, out, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                              draft_lens, max_context_len, sm_scale, num_splits=0, workspace=None, stream=None):
+    """splash_kv_append_int8 and splash_verify_attn in one call: the drafted block's
+    K/V rows come from k_new / v_new ([B][T_max][Hkv][D], fp32 or bf16), are
+    quantised in the kernel as the append quantises them, attended, and stored
+    into the pools' block slots (the pools end byte-identical to the append's)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B][T_max][Hq][D]")
+    B, T_max, Hq, Dq = q.shape
+    _dev(q, "q", (torch.bfloat16, torch.int16))
+    _dev(out, "out", (torch.bfloat16, torch.int16), tuple(q.shape))
+    num_pages, Hkv, P, D = _pool_dims(k_pool, v_pool, k_scale, v_scale)
+    if Dq != D:
+        raise ValueError("q head dim does not match the pools")
+    _dev(k_new, "k_new", (torch.float32, torch.bfloat16), (B, T_max, Hkv, D))
+    _dev(v_new, "v_new", (k_new.dtype,), (B, T_max, Hkv, D))
+    maxp = _lens(block_table, context_lens, draft_lens, B)
+    S_req = num_splits if num_splits > 0 else (
+        splash_verify_attn_default_splits(B, Hkv, max_context_len, P, D) if B and max_context_len else 1)
+    S = effective_splits(max_context_len, P, S_req) if max_context_len else 1
+    need = splash_verify_attn_workspace_bytes(B, T_max, Hq, D, S)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _dev(workspace, "workspace", (torch.uint8, torch.int8, torch.float32))
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    src = SPLASH_SRC_F32 if k_new.dtype == torch.float32 else SPLASH_SRC_BF16
+    rc = _lib().splash_verify_attn_append(
+        k_new.data_ptr(), v_new.data_ptr(), src, q.data_ptr(), out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        k_scale.data_ptr(), v_scale.data_ptr(), block_table.data_ptr(), maxp, context_lens.data_ptr(),
+        draft_lens.data_ptr(), B, T_max, Hq, Hkv, D, P, num_pages, int(max_context_len), float(sm_scale),
+        int(S_req), ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "splash_verify_attn_append")
+    return out
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20                    # SPLASH_NOALLOC_SCRATCH_BYTES

@@ -158,13 +158,21 @@ size_t splash_verify_attn_workspace_bytes(int B, int T_max, int Hq, int D, int n
            align_up((size_t)B * Hq * num_splits * sizeof(int), 256);
 }
 
+// the drafted block's source rows (the call that appends and verifies; the
+// pools it is stored into are the call's own, writable there)
+struct BlockAppend {
+    const void* k_new;
+    const void* v_new;
+    bool src_bf16;
+};
+
 static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,
                             const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
                             int max_pages_per_seq, const int32_t* context_lens, const int32_t* draft_lens,
                             int B, int T_max, int Hq, int Hkv, int D, int P, int num_pages,
                             int max_context_len, float sm_scale, int num_splits, void* workspace,
                             size_t workspace_bytes, void* stream, const uint32_t* block_masks,
-                            int window, bool prefill = false) {
+                            int window, bool prefill = false, const BlockAppend* app = nullptr) {
     // a prefill chunk runs as ceil(T_max / 16) verify blocks per request
     const int nblk = prefill ? ceil_div(T_max, kMaxVerifyT) : 1;
     if (prefill && (T_max < 0 || (long)B * nblk > 65535)) return SPLASH_ERR_INVALID_ARGUMENT;
@@ -190,6 +198,11 @@ static int verify_attn_impl(const uint16_t* q, uint16_t* out, const int8_t* k_po
     a.block_masks = block_masks;
     a.window = window;
     a.blocks_per_req = nblk;
+    if (app != nullptr) {
+        a.k_src = app->k_new;
+        a.v_src = app->v_new;
+        a.src_bf16 = app->src_bf16;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (S == 1) {
         a.out = out;
@@ -221,6 +234,24 @@ int splash_verify_attn(const uint16_t* q, uint16_t* out, const int8_t* k_pool, c
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
                             context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
                             sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int splash_verify_attn_append(const void* k_new, const void* v_new, int src_dtype, const uint16_t* q, uint16_t* out,
+                              int8_t* k_pool, int8_t* v_pool, uint16_t* k_scale, uint16_t* v_scale,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* context_lens, const int32_t* draft_lens, int B, int T_max, int Hq,
+                              int Hkv, int D, int P, int num_pages, int max_context_len, float sm_scale,
+                              int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!k_new || !v_new) return SPLASH_ERR_INVALID_ARGUMENT;
+    if (src_dtype != SPLASH_SRC_F32 && src_dtype != SPLASH_SRC_BF16) return SPLASH_ERR_INVALID_ARGUMENT;
+    // fp32 rows are read 16 bytes a lane at D = 256 (as the append reads them)
+    const size_t elem = src_dtype == SPLASH_SRC_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % (elem * (D / 64 > 0 ? D / 64 : 1)))
+        return SPLASH_ERR_INVALID_ARGUMENT;
+    const BlockAppend app{k_new, v_new, src_dtype == SPLASH_SRC_BF16};
+    return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,
+                            context_lens, draft_lens, B, T_max, Hq, Hkv, D, P, num_pages, max_context_len,
+                            sm_scale, num_splits, workspace, workspace_bytes, stream, nullptr, 0, false, &app);
 }
 
 int splash_verify_attn_noalloc(const uint16_t* q, uint16_t* out, const int8_t* k_pool, const int8_t* v_pool,

@@ -31,19 +31,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Wave-wide reductions over all 64 lanes (result in every lane).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
 // gfx950 lane-swap instructions.  Swapping a register with itself exchanges the
 // odd 16-lane rows of one copy with the even rows of the other, so the two
@@ -73,6 +60,22 @@ __device__ __forceinline__ float group4_sum(float v) {
     lane_swap16(v, a, b);
     lane_swap32(a + b, a, b);
     return a + b;
+}
+
+// Maximum over all 64 lanes, in every lane: inside each 16-lane row with DPP
+// moves (quad exchanges, then rotations by 4 and 8 lanes), across the rows with
+// the lane swaps; all register moves, none through the LDS.  The maximum does
+// not depend on the order it is taken in.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, bit_cast<float>(__builtin_amdgcn_update_dpp(0u, bit_cast<uint32_t>(v), CTRL, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = dpp_max<0xb1>(v);                            // quad_perm [1, 0, 3, 2]
+    v = dpp_max<0x4e>(v);                            // quad_perm [2, 3, 0, 1]
+    v = dpp_max<0x124>(v);                           // row_ror 4
+    v = dpp_max<0x128>(v);                           // row_ror 8
+    return group4_max(v);
 }
 
 }  // namespace splash

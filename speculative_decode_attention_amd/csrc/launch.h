@@ -47,6 +47,13 @@ struct VerifyArgs {
     const uint32_t* block_masks = nullptr;   // [B][T_max] bit u of row t: draft t sees draft u; null: causal
     int window = 0;                          // > 0: draft at position p sees keys p - window < j <= p
     int blocks_per_req = 1;                  // > 1: a prefill chunk cut into 16-token blocks, B counts blocks
+    // non-null: the call appends the drafted block too: its K and V rows come
+    // from these source rows ([B][T_max][Hkv][D], fp32 or bf16), quantised as
+    // the append quantises them, instead of from the pools' slots of the block,
+    // and are stored into the pools (then the caller's writable pools)
+    const void* k_src = nullptr;
+    const void* v_src = nullptr;
+    bool src_bf16 = false;
 };
 
 // Merge of fp32 partial rows in the exported layout: part_o [B][Hq][T_max][S][D],

@@ -38,6 +38,7 @@ __device__ __forceinline__ void load_row(const void* src, size_t off, float (&x)
 // little-endian (code e in byte e) and the binary16 scale bits.
 template <int D>
 __device__ __forceinline__ uint32_t quantize_row(const float (&x)[D / 64], uint16_t& s16_bits) {
+#pragma clang fp contract(off)
     constexpr int E = D / 64;
     float amax = 0.0f;
 #pragma unroll
@@ -47,15 +48,24 @@ __device__ __forceinline__ uint32_t quantize_row(const float (&x)[D / 64], uint1
     const _Float16 s16 = (_Float16)s32;              // round to nearest even
     const float s = (float)s16;                      // exact widening
     s16_bits = bit_cast<uint16_t>(s16);
+    // an all-zero row (s = 0) has all-zero codes: divide by 1 and select 0,
+    // without a branch
+    const bool zero = s == 0.0f;
+    const float sd = zero ? 1.0f : s;
+    // x / s correctly rounded with one division per row: r = RN(1 / s) (an
+    // IEEE division), q0 = RN(x r), the residual x - q0 s is exact on an FMA,
+    // and RN(q0 + residual r) is RN(x / s) (Markstein's theorem for division
+    // with a correctly rounded reciprocal; no underflow matters here, since
+    // |x / s| < 1/2 whenever x is subnormal)
+    const float r = 1.0f / sd;
     uint32_t packed = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        int c = 0;
-        if (s != 0.0f) {
-            float r = __builtin_rintf(x[e] / s);     // IEEE division, ties to even
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            c = (int)r;
-        }
+        const float q0 = x[e] * r;
+        const float q = __builtin_fmaf(__builtin_fmaf(-q0, sd, x[e]), r, q0);
+        float k = __builtin_rintf(q);                 // ties to even
+        k = fminf(fmaxf(k, -127.0f), 127.0f);
+        const int c = zero ? 0 : (int)k;
         packed |= ((uint32_t)(c & 0xff)) << (8 * e);
     }
     return packed;

@@ -59,6 +59,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace splash {
 
@@ -70,7 +71,10 @@ constexpr int kIdRing = 8;
 // how a draft sees the block and the context: the causal chain, a tree of
 // candidates (per-draft bit masks), a sliding window over the keys, or the
 // causal chain of a prefill chunk cut into several 16-token blocks per request
-constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2, kMaskChunked = 3;
+constexpr int kMaskCausal = 0, kMaskTree = 1, kMaskWindow = 2, kMaskChunked = 3, kMaskAppend = 4;
+// the append mode: a split of at least this many steps stores the block's rows
+// into the pools early enough that its own copies of them need no wait
+constexpr int kAppendEarlySteps = 6;
 
 // A work item's request.  Verify: request b itself.  A prefill chunk of
 // n_b tokens is cut into blocks of 16 (blocks_per_req of them per request):
@@ -222,13 +226,18 @@ struct Cfg {
     static constexpr int R_OFF = M_OFF + NT * 16 * kPagesPerIter * 4;   // [row] O rescale factors / references
     static constexpr int MASK_OFF = R_OFF + NT * 16 * 4;          // [16] block masks of the request's drafts
     static constexpr int TOTAL = MASK_OFF + 16 * 4;
+    // the append mode only: the block's V codes by token, [16][D] bytes, then
+    // its K and V scales by token, [16] + [16] fp16
+    static constexpr int STG_OFF = TOTAL;
+    static constexpr int STG_S_OFF = STG_OFF + kPage * D;
+    static constexpr int TOTAL_APPEND = STG_S_OFF + 2 * kPage * 2;
     static constexpr int Q_OFF = V_OFF + SLOT;        // start-up only: Q over the V slots 1.. onwards
     static constexpr int QBYTES = NT * 16 * D * 2;
     static_assert(D % 64 == 0 && PVW >= 1, "head dim must be a multiple of 64");
     static_assert(NT % 2 == 0, "the two row halves hold whole tiles");
     static_assert(PAGE % 1024 == 0, "page must be whole 1 KB copies");
     static_assert(Q_OFF + QBYTES <= TOTAL, "Q staging does not fit");
-    static_assert(TOTAL <= 160 * 1024, "LDS arena exceeds 160 KB");
+    static_assert(TOTAL_APPEND <= 160 * 1024, "LDS arena exceeds 160 KB");
 };
 
 // XOR swizzle of 16-byte chunks inside a K row, by slot: the 16 lanes reading
@@ -321,6 +330,63 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         }
     }
 
+    // ---- kMaskAppend: the call appends the drafted block too.  The block ends
+    // the context, so its pages pA and pB = pA or pA + 1 are the last page or
+    // two of the split holding them.  In such a split the score waves, idle
+    // while Q and the first pages are in flight, quantise the block's rows
+    // exactly as the append does (score wave v: the K and V rows of tokens
+    // 4 v .. 4 v + 3) and store them into the pools' slots of the split's
+    // pages: K rows directly, V rows through the LDS, each 8-byte word of the
+    // [2][D][8] V pages that holds a block slot being read, merged and written
+    // back whole after the barrier before the loop.  The stores have
+    // completed before the barrier of step 1, and the block's pages are copied
+    // after it when the split has kAppendEarlySteps steps or more (they are
+    // then in step n - 2 or later, copied from step n - 5 on), so the copies
+    // read the appended rows.  A shorter split ("late") issues its first page
+    // copies only after one more barrier, which the score waves reach once
+    // their stores have completed.  The source rows reach the LDS as direct
+    // copies, K rows at the end of the P' buffers, V rows in the K ring slot
+    // of step kKAhead, both unused before the loop: copies the compiler does
+    // not track, so it adds no wait of its own for them (a tracked load would
+    // make it wait for every page copy).
+    bool blk = false, late = false;
+    int idA = -1, idB = -1;
+    // the append mode, score waves: the pool's V words holding block slots
+    // (up to three 8-slot groups of D words, VW per lane)
+    constexpr int VW = (3 * D + 255) / 256;
+    uint64_t vword[VW];
+    constexpr int EQ = D / 64;
+    constexpr int SRC_STRIDE = 4 * D * 4;                     // one wave's four fp32 rows
+    constexpr int SRC_K_OFF = C::P_OFF + 2 * C::PBUF - 4 * SRC_STRIDE;
+    static_assert(C::Q_OFF + C::QBYTES <= SRC_K_OFF && SRC_K_OFF >= C::P_OFF && 4 * SRC_STRIDE <= C::SLOT,
+                  "source rows do not fit");
+    const int tw = v & 3;                                     // this wave's token group
+    const uint32_t src_k = SRC_K_OFF + tw * SRC_STRIDE;
+    const uint32_t src_v = C::K_OFF + (kKAhead & (kRing - 1)) * C::SLOT + tw * SRC_STRIDE;
+    if constexpr (MASK == kMaskAppend) {
+        const int pA = (ctx - dl) / kPage, pB = (ctx - 1) / kPage;
+        const bool inA = pA >= pg_begin && pA < pg_end, inB = pB >= pg_begin && pB < pg_end;
+        blk = inA || inB;
+        late = blk && n < kAppendEarlySteps;
+        if (blk) {
+            if (scorer) {
+                const const_i32_ptr row = (const_i32_ptr)(a.block_table + (size_t)br * a.max_pages_per_seq);
+                if (inA) idA = row[pA];
+                if (inB) idB = row[pB];
+            }
+            const int row16 = a.src_bf16 ? D / 8 : D / 4;     // 16-byte pieces of a source row
+            const int esz = a.src_bf16 ? 2 : 4;
+#pragma unroll
+            for (int k = 0; k < SRC_STRIDE / 1024; ++k) {
+                const int ch = 64 * k + lane, u = ch / row16, t = 4 * tw + u;
+                const size_t off = ((((size_t)br * a.T_max + t) * a.Hkv + g) * D) * esz + 16 * (ch % row16);
+                if (scorer && u < 4 && t < dl) {
+                    dma16_to_lds(static_cast<const uint8_t*>(a.k_src) + off, lds_base + src_k + 1024 * k);
+                    dma16_to_lds(static_cast<const uint8_t*>(a.v_src) + off, lds_base + src_v + 1024 * k);
+                }
+            }
+        }
+    }
     // per-lane byte offsets of the K copies inside a page (rows XOR-swizzled by chunk)
     auto koff = [&](int i) -> int {
         const int ch = 64 * i + lane;
@@ -367,13 +433,93 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         if (MASK == kMaskTree && c == 1 && lane < 16)         // the drafts' block masks
             *reinterpret_cast<uint32_t*>(lds + C::MASK_OFF + 4 * lane) =
                 lane < a.T_max ? a.block_masks[(size_t)br * a.T_max + lane] : 0u;
+        if (!late) {
 #pragma unroll
-        for (int j = 0; j < kKAhead; ++j) issue_k(j, clamp_page(idj[j]));
-        issue_v(0, clamp_page(idj[0]));
-        // this lane's Q chunks have landed (only the page copies may be in flight)
-        wait_vmcnt<3 * KC_START + NI>();
+            for (int j = 0; j < kKAhead; ++j) issue_k(j, clamp_page(idj[j]));
+            issue_v(0, clamp_page(idj[0]));
+            // this lane's Q chunks (and block source rows) have landed (only
+            // the page copies may be in flight)
+            wait_vmcnt<3 * KC_START + NI>();
+        } else {
+            wait_vmcnt<0>();
+        }
     } else {
         wait_vmcnt<0>();
+        if constexpr (MASK == kMaskAppend) {
+            if (blk) {
+                // This wave's tokens: K rows and V rows, each read from its
+                // LDS copy and quantised as the append quantises it.  K rows
+                // (D contiguous bytes) are stored now; V codes and all scales
+                // go to the LDS staging area, for the V words to be built
+                // after the barrier: a V page is [2][D][8] (8-token groups,
+                // d-major), and single-byte stores scattered over it cost
+                // hundreds of cycles each, so every 8-byte word holding a
+                // block slot is read from the pool, merged and written back
+                // whole.  Those words are loaded first, so their latency
+                // overlaps the quantisation.  A token of a page outside this
+                // split, or a page id outside the pool, is skipped.
+                const int sA = (ctx - dl) % kPage;            // the block's first slot in page pA
+                const int nvg = (sA + dl - 1) / 8 - sA / 8 + 1;   // 8-slot groups it touches (<= 3)
+                uint64_t* const word = vword;
+#pragma unroll
+                for (int k = 0; k < VW; ++k) {
+                    const int i = 64 * (tw + 4 * k) + lane, vg = sA / 8 + i / D, d = i % D;
+                    const int id = vg < 2 ? idA : idB;
+                    word[k] = 0;
+                    if (i / D < nvg && id >= 0 && id < a.num_pages)
+                        word[k] = *reinterpret_cast<const uint64_t*>(
+                            a.v_pool + ((size_t)id * a.Hkv + g) * C::PAGE + ((vg & 1) * D + d) * 8);
+                }
+                int8_t* const kp = const_cast<int8_t*>(a.k_pool);         // writable in this mode
+                const int pA = (ctx - dl) / kPage;
+                float x[8][EQ];
+                if (a.src_bf16) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const uint16_t* px = reinterpret_cast<const uint16_t*>(lds + (r < 4 ? src_k : src_v) + (r & 3) * D * 2) + lane * EQ;
+#pragma unroll
+                        for (int e = 0; e < EQ; ++e) x[r][e] = bit_cast<float>((uint32_t)px[e] << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const float* px = reinterpret_cast<const float*>(lds + (r < 4 ? src_k : src_v) + (r & 3) * D * 4) + lane * EQ;
+#pragma unroll
+                        for (int e = 0; e < EQ; ++e) x[r][e] = px[e];
+                    }
+                }
+                uint32_t q8[8];
+                uint16_t s8[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const bool in = 4 * tw + (r & 3) < dl;
+#pragma unroll
+                    for (int e = 0; e < EQ; ++e) x[r][e] = in ? x[r][e] : 0.0f;
+                    q8[r] = quantize_row<D>(x[r], s8[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int u = r & 3, t = 4 * tw + u, pos = ctx - dl + t;
+                    if (t >= dl) continue;
+                    if (lane == 0)
+                        reinterpret_cast<uint16_t*>(lds + C::STG_S_OFF)[(r < 4 ? 0 : kPage) + t] = s8[r];
+                    if (r < 4) {
+                        const int id = pos / kPage == pA ? idA : idB;
+                        if (id >= 0 && id < a.num_pages) {
+                            int8_t* const kdst = kp + (((size_t)id * a.Hkv + g) * kPage + pos % kPage) * D + lane * EQ;
+                            if constexpr (EQ == 4) *reinterpret_cast<uint32_t*>(kdst) = q8[r];
+                            else if constexpr (EQ == 2) *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)q8[r];
+                            else *kdst = (int8_t)q8[r];
+                        }
+                    } else {
+                        uint8_t* const row = lds + C::STG_OFF + t * D + lane * EQ;
+                        if constexpr (EQ == 4) *reinterpret_cast<uint32_t*>(row) = q8[r];
+                        else if constexpr (EQ == 2) *reinterpret_cast<uint16_t*>(row) = (uint16_t)q8[r];
+                        else *row = (uint8_t)q8[r];
+                    }
+                }
+            }
+        }
     }
     // bf16 -> fp16 in place, each lane its own chunks (exact for 2^-17 <= |q| <= 65504);
     // padded rows become q = 0.  All reads first, then all writes.
@@ -401,6 +547,50 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         }
     }
     lds_barrier();
+    if constexpr (MASK == kMaskAppend) {
+        if (scorer && blk) {
+            // the V words: the block's codes of each word's slots, from the
+            // staging area, over the pool's bytes of the others; then the
+            // block's K and V scales (score wave 0, lanes 0-31)
+            int8_t* const vp = const_cast<int8_t*>(a.v_pool);             // writable in this mode
+            const int sA = (ctx - dl) % kPage;
+            const int nvg = (sA + dl - 1) / 8 - sA / 8 + 1;
+#pragma unroll
+            for (int k = 0; k < VW; ++k) {
+                const int i = 64 * (tw + 4 * k) + lane, vg = sA / 8 + i / D, d = i % D;
+                const int id = vg < 2 ? idA : idB;
+                if (i / D >= nvg || id < 0 || id >= a.num_pages) continue;
+                uint64_t w = vword[k];
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const int t = 8 * vg + b - sA;            // block token of this slot
+                    if (t >= 0 && t < dl) {
+                        const uint64_t code = lds[C::STG_OFF + t * D + d];
+                        w = (w & ~(0xffull << (8 * b))) | (code << (8 * b));
+                    }
+                }
+                *reinterpret_cast<uint64_t*>(vp + ((size_t)id * a.Hkv + g) * C::PAGE + ((vg & 1) * D + d) * 8) = w;
+            }
+            if (v == 0 && lane < 2 * kPage) {
+                const int t = lane & (kPage - 1), pos = ctx - dl + t;
+                const int id = pos / kPage == (ctx - dl) / kPage ? idA : idB;
+                if (t < dl && id >= 0 && id < a.num_pages) {
+                    uint16_t* const sc = const_cast<uint16_t*>(lane < kPage ? a.k_scale : a.v_scale);
+                    sc[((size_t)id * a.Hkv + g) * kPage + pos % kPage] =
+                        reinterpret_cast<const uint16_t*>(lds + C::STG_S_OFF)[lane];
+                }
+            }
+            if (late) wait_vmcnt<0>();                        // before the barrier the first copies wait on
+        }
+        if (late) {
+            lds_barrier();
+            if (!scorer) {                                    // the first copies, now that the block is stored
+#pragma unroll
+                for (int j = 0; j < kKAhead; ++j) issue_k(j, clamp_page(idj[j]));
+                issue_v(0, clamp_page(idj[0]));
+            }
+        }
+    }
 
     if (scorer) {
         // ================= score waves =================
@@ -490,6 +680,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         const float zscale = a.sm_scale * kLog2e;
 
         for (int it = 0; it < n + 2; ++it) {
+            // the append mode: this wave's pool stores have completed before
+            // the barrier of step 1, after which the block's pages may be copied
+            if (MASK == kMaskAppend && it == 1) wait_vmcnt<0>();
             // the K pages of step it, the flags of step it - 1 and (for the
             // output waves) the P' tiles of step it - 2 are published
             lds_barrier();
@@ -967,7 +1160,8 @@ __device__ __forceinline__ void dispatch_tiles(int nt_used, const VerifyArgs& a,
 template <int D, int G, int MASK>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void verify_partition_kernel(const VerifyArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg<D, G>::TOTAL];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MASK == kMaskAppend ? Cfg<D, G>::TOTAL_APPEND
+                                                                               : Cfg<D, G>::TOTAL];
 
     // work item: blockIdx.x = (b * Hkv + g) * S + s  (equal (g, s) of different
     // requests sit S * Hkv apart, so they share an XCD when that is a multiple of 8)
@@ -1239,6 +1433,8 @@ static hipError_t launch_partition_dg(const VerifyArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskTree>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     else if (a.window > 0)
         hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskWindow>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+    else if (a.k_src != nullptr)
+        hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskAppend>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((verify_partition_kernel<D, G, kMaskCausal>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
