@@ -927,6 +927,16 @@ def summarize_traffic(fetch_dir, write_dir, phase_log, cmd):
     print(f"\nPer call: {fb_call / 1e6:.2f} MB fetched + {wb_call / 1e6:.2f} MB written = "
           f"{(fb_call + wb_call) / 1e6:.2f} MB against {verify_bytes(32768, 4, 256, 16, 24) / 1e6:.2f} MB "
           "algorithmic.")
+    # the partition kernel by phase of the run (every workload the run timed)
+    pf = [v for _, k, v in fetch if PART_KERNEL in k]
+    pw = [v for _, k, v in write if PART_KERNEL in k]
+    print(f"\nThe `{_short(PART_KERNEL)}` launches by phase of the run (scaled as above):\n")
+    print("| phase | launches | fetched MB per launch | written MB per launch |")
+    print("|---|---:|---:|---:|")
+    for name, i0, i1 in _phase_slices(phase_log, len(pf)):
+        if i1 > i0:
+            print(f"| {name} | {i1 - i0} | {np.mean(pf[i0:i1]) * 1024 * f_fac / 1e6:.2f} | "
+                  f"{np.mean(pw[i0:i1]) * 1024 * w_fac / 1e6:.2f} |")
     print("\nRecord read by bench.py (`roofline.traffic`, only while the source hash matches):\n")
     print(json.dumps(rec))
 
