@@ -36,25 +36,32 @@
 //    sum_d q_d (1152 + x_d) comes out unbiased; for V the bias is subtracted
 //    exactly with a packed fp16 add before the MFMA.
 //  * Scores are kept relative to a per-row reference m that moves lazily: only
-//    when a step's maximum exceeds it by more than tau (log2 units, 8 unless a
-//    V scale of the step exceeds 255, then 0), so p = exp2(z - m) <= 2^tau and
-//    P' = p * s_v stays inside fp16.  Each score wave publishes one flag byte
-//    per step; without a flag no reference moves and nothing is exchanged.  The
-//    first references are the exact maxima of step 0, exchanged across the
-//    barrier that already separates steps 0 and 1.
+//    when a step's maximum exceeds it by more than tau = 8 (log2 units), so
+//    p = exp2(z - m) <= 2^tau.  Weights are carried as p 2^jv in fp32, with the
+//    workgroup's V exponent jv set so that the largest V scale seen times 2^jv
+//    lies in [64, 128): P' = p 2^jv s_v is then one fp16 rounding, inside fp16
+//    whatever the V scales.  Each score wave publishes one flag per step (a
+//    score past its slack, or a V scale in a higher binade than jv allows);
+//    without a flag nothing moves and nothing is exchanged.  The first
+//    references and jv come from the exact maxima of step 0, exchanged across
+//    the barrier that already separates steps 0 and 1.
 //  * Q K^T uses v_mfma_f32_16x16x32_f16 (S^T = K Q^T, one 16-key page x 16 rows
 //    per tile); P V uses v_mfma_f32_32x32x16_f16 (O^T = V^T P'^T, 32 columns x
 //    32 rows x 16 keys).  No AGPR is used: a wave then has 256 VGPRs for the
 //    queries (score waves) or the O accumulators (output waves) and the working
 //    set.
-//  * The epilogue divides by the row sums and writes bf16 rows (one split) or
-//    fp16 partial tiles with their natural-log log-sum-exp (several splits).
+//  * The epilogue divides by the row sums and writes bf16 rows (one split),
+//    fp32 partial rows (the exported partition call) or fp16 partial tiles
+//    times 2^jv with jv beside them (several splits inside the verify call),
+//    with their natural-log log-sum-exp.
 //  * Visibility is a compile-time mode of the kernel, so each variant keeps
 //    its own straight-line step: the causal chain; a tree of candidates (bit
 //    masks per draft, staged in LDS); a sliding window of the last W keys
 //    (splits start at the first visible page); and the causal chain of a
 //    prefill chunk cut into 16-token blocks, each a verify block over the cache
-//    up to its own last token.
+//    up to its own last token.  A fifth mode is the causal chain whose call also
+//    appends the drafted block (its rows quantised and stored by the workgroup
+//    that holds their pages, before it copies them).
 #include <math.h>
 
 #include "device.h"
