@@ -174,3 +174,13 @@ def test_append_verify_step_captured_and_replayed():
         assert np.array_equal(out.cpu().numpy(), want), f"replay {rep}: differs from append + verify"
         assert_pools(pools, prep.pools, f"replay {rep}")
     log("  captured append + verify step: 3 replays identical to append + verify, pools equal to the oracle's")
+
+
+@pytest.mark.parametrize("S", [1, 2, 0])
+def test_append_verify_short_contexts_and_empty_blocks(S):
+    """A context that is its block (no key before it), a block straddling pages 0
+    and 1, a request with no block (a no-op: its pages stay as they were), a
+    one-token block, and a block filling page 2 exactly."""
+    prep = prepared("drafts_short", B=5, context_lens=[16, 17, 9, 3, 48], T_max=16, draft_lens=[16, 5, 0, 1, 16],
+                    Hq=24, Hkv=4, D=256, num_pages=64)
+    check_against_append(prep, S, f"short contexts, {S or 'preset'} splits")
