@@ -244,9 +244,12 @@ int splash_verify_attn_append(const void* k_new, const void* v_new, int src_dtyp
                               int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
     if (!k_new || !v_new) return SPLASH_ERR_INVALID_ARGUMENT;
     if (src_dtype != SPLASH_SRC_F32 && src_dtype != SPLASH_SRC_BF16) return SPLASH_ERR_INVALID_ARGUMENT;
-    // fp32 rows are read 16 bytes a lane at D = 256 (as the append reads them)
+    // a lane reads D / 64 consecutive source values at once (16 bytes of fp32 at
+    // D = 256, as the append reads them); a shape outside the compiled set is
+    // refused by the verify checks below
     const size_t elem = src_dtype == SPLASH_SRC_F32 ? 4 : 2;
-    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % (elem * (D / 64 > 0 ? D / 64 : 1)))
+    if (append_supported(D) &&
+        (reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) % (elem * (D / 64)))
         return SPLASH_ERR_INVALID_ARGUMENT;
     const BlockAppend app{k_new, v_new, src_dtype == SPLASH_SRC_BF16};
     return verify_attn_impl(q, out, k_pool, v_pool, k_scale, v_scale, block_table, max_pages_per_seq,

@@ -203,3 +203,37 @@ def test_accept_rejects_bad_arguments(lib):
 def test_binding_fails_loudly_without_the_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         sda.load_library(tmp_path / "missing.so")
+
+
+def _append_verify(lib, **over):
+    a = dict(k=FAKE, v=FAKE, src=0, q=FAKE, out=FAKE, k_pool=FAKE, v_pool=FAKE, ks=FAKE, vs=FAKE, bt=FAKE,
+             maxp=2048, ctx=FAKE, dl=FAKE, B=1, T=16, Hq=24, Hkv=4, D=256, P=16, num_pages=65536,
+             max_ctx=32768, sm=0.0625, S=0, ws=None, ws_bytes=0)
+    a.update(over)
+    return lib.splash_verify_attn_append(a["k"], a["v"], a["src"], a["q"], a["out"], a["k_pool"], a["v_pool"],
+                                         a["ks"], a["vs"], a["bt"], a["maxp"], a["ctx"], a["dl"], a["B"], a["T"],
+                                         a["Hq"], a["Hkv"], a["D"], a["P"], a["num_pages"], a["max_ctx"],
+                                         ctypes.c_float(a["sm"]), a["S"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=None), sda.SPLASH_ERR_INVALID_ARGUMENT),            # no source rows
+    (dict(v=None), sda.SPLASH_ERR_INVALID_ARGUMENT),
+    (dict(src=2), sda.SPLASH_ERR_INVALID_ARGUMENT),             # unknown source dtype
+    (dict(k=FAKE + 4), sda.SPLASH_ERR_INVALID_ARGUMENT),        # fp32 rows read 16 bytes a lane at D = 256
+    (dict(src=1, v=FAKE + 2), sda.SPLASH_ERR_INVALID_ARGUMENT),  # bf16 rows read 8 bytes a lane
+    (dict(q=None), sda.SPLASH_ERR_INVALID_ARGUMENT),            # then everything the verify call checks
+    (dict(maxp=100), sda.SPLASH_ERR_INVALID_ARGUMENT),
+    (dict(T=17), sda.SPLASH_ERR_UNSUPPORTED),
+    (dict(D=192), sda.SPLASH_ERR_UNSUPPORTED),
+    (dict(S=64, ws=None), sda.SPLASH_ERR_INVALID_ARGUMENT),
+    (dict(S=64, ws=FAKE, ws_bytes=1024), sda.SPLASH_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_append_verify_rejects_bad_arguments(lib, over, status):
+    assert _append_verify(lib, **over) == status
+
+
+def test_append_verify_empty_is_a_no_op(lib):
+    assert _append_verify(lib, B=0) == sda.SPLASH_OK
+    assert _append_verify(lib, T=0) == sda.SPLASH_OK
+    assert _append_verify(lib, max_ctx=0) == sda.SPLASH_OK
