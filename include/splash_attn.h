@@ -123,8 +123,10 @@ int splash_kv_append_int8(const void* k_new, const void* v_new, int src_dtype,
  * splash_verify_attn_default_splits -- the split-K preset: how many context
  * splits one request's pages are cut into so that B * Hkv * splits work items
  * fill the device's compute units (presets keyed by core count, as the
- * summary's Metal-kernels section describes).  Returns >= 1, or a negative
- * status on bad arguments or a failed device query.
+ * summary's Metal-kernels section describes), with at least 8 pages a split
+ * (4 at D = 256 up to 64 pages of context; one split at D = 64 up to 16
+ * pages, where the merge launch costs more than it saves).  Returns >= 1, or a
+ * negative status on bad arguments or a failed device query.
  */
 int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P, int D);
 

@@ -23,8 +23,14 @@ constexpr int kMaxVerifyT = 16;
 constexpr int kMaxAcceptT = 64;     // the finalize kernel keeps a block on one wave
 constexpr int kMaxAcceptV = 1 << 30;
 // smallest number of pages a split is given by the preset: below this the
-// fixed cost of a workgroup (loading Q, writing partials) dominates its work
+// fixed cost of a workgroup (loading Q, writing partials) dominates its work.
+// Measured on MI355X (verify call, one request, 24 q / 4 kv heads): at D = 256
+// one step of 4 pages per split is the fastest up to 64 pages of context
+// (256 tokens: 13.5 against 15.9 us with 8 pages a split; 1K tokens: 14.5
+// against 16.2 us), 8 pages from 2K tokens on; at D = 64 a single split (no
+// merge launch) is the fastest up to 16 pages (256 tokens: 7.4 against 9.4 us).
 constexpr int kMinPagesPerSplit = 8;
+constexpr int kMinPagesShortD256 = 4, kShortContextPages = 64, kOneSplitPagesD64 = 16;
 
 std::mutex g_cu_mutex;
 int g_cu_count[kMaxDevices] = {0};
@@ -143,7 +149,8 @@ int splash_verify_attn_default_splits(int B, int Hkv, int max_context_len, int P
     const long items = (long)B * Hkv;
     int S = ceil_div(cus, items);                         // one workgroup per compute unit
     const int n_pages = ceil_div(max_context_len, P);
-    const int cap = ceil_div(n_pages, kMinPagesPerSplit);
+    const int min_pages = D >= 256 && n_pages <= kShortContextPages ? kMinPagesShortD256 : kMinPagesPerSplit;
+    const int cap = D <= 64 && n_pages <= kOneSplitPagesD64 ? 1 : ceil_div(n_pages, min_pages);
     if (S > cap) S = cap;
     return S < 1 ? 1 : S;
 }
