@@ -162,3 +162,20 @@ def test_merge_is_deterministic_and_order_fixed():
     assert np.array_equal(a, out.cpu().numpy())
     want = torch.from_numpy(np.ascontiguousarray(po[..., 17, :].transpose(0, 2, 1, 3))).to(torch.bfloat16)
     assert np.array_equal(a, want.view(torch.int16).numpy())
+
+
+@pytest.mark.parametrize("B,Hkv,ctx,D,cap", [
+    (1, 2, 256, 64, 1),           # config 1: 16 pages at D = 64, one split (no merge launch)
+    (1, 2, 512, 64, 4),           # 32 pages at D = 64: 8 pages a split
+    (1, 4, 256, 256, 4),          # 16 pages at D = 256: one 4-page step a split
+    (1, 4, 1024, 256, 16),        # 64 pages at D = 256: still 4 pages a split
+    (1, 4, 2048, 256, 16),        # 128 pages: 8 pages a split again
+    (1, 4, 32768, 256, 256),      # config 3
+    (16, 4, 32768, 256, 256),     # config 5
+])
+def test_split_preset(B, Hkv, ctx, D, cap):
+    """The split preset: one workgroup per compute unit over B * Hkv work items,
+    capped by the pages a split must at least hold (the cap column)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = max(1, min(-(-cus // (B * Hkv)), cap))
+    assert sda.splash_verify_attn_default_splits(B, Hkv, ctx, 16, D) == want
