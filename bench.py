@@ -937,6 +937,21 @@ def summarize_traffic(fetch_dir, write_dir, phase_log, cmd):
         if i1 > i0:
             print(f"| {name} | {i1 - i0} | {np.mean(pf[i0:i1]) * 1024 * f_fac / 1e6:.2f} | "
                   f"{np.mean(pw[i0:i1]) * 1024 * w_fac / 1e6:.2f} |")
+    # every library kernel of the run, whatever workload launched it (the
+    # prefill leg's chunked partition and merge, the D = 64 kernels of config 1)
+    fall, wall = {}, {}
+    for _, k, v in fetch:
+        if "splash::" in k:
+            fall.setdefault(_short(k), []).append(v)
+    for _, k, v in write:
+        if "splash::" in k:
+            wall.setdefault(_short(k), []).append(v)
+    print("\nEvery library kernel of the run, per dispatch (scaled as above):\n")
+    print("| kernel | dispatches | fetched MB per dispatch | written MB per dispatch |")
+    print("|---|---:|---:|---:|")
+    for k in sorted(fall):
+        print(f"| `{k}` | {len(fall[k])} | {np.mean(fall[k]) * 1024 * f_fac / 1e6:.2f} | "
+              f"{np.mean(wall.get(k, [0.0])) * 1024 * w_fac / 1e6:.2f} |")
     print("\nRecord read by bench.py (`roofline.traffic`, only while the source hash matches):\n")
     print(json.dumps(rec))
 
