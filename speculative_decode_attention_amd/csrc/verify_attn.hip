@@ -339,11 +339,11 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
 
     // ---- kMaskAppend: the call appends the drafted block too.  The block ends
     // the context, so its pages pA and pB = pA or pA + 1 are the last page or
-    // two of the split holding them.  In such a split the waves, idle while
-    // Q and the first pages are in flight, quantise the block's rows exactly
-    // as the append does (score wave v the K rows of tokens 4 v .. 4 v + 3,
-    // output wave 4 + v their V rows) and store them into the pools' slots of
-    // the split's pages: K rows directly, V rows through the LDS, each 8-byte word of the
+    // two of the split holding them.  In such a split the score waves, idle
+    // while Q and the first pages are in flight, quantise the block's rows
+    // exactly as the append does (score wave v: the K and V rows of tokens
+    // 4 v .. 4 v + 3) and store them into the pools' slots of the split's
+    // pages: K rows directly, V rows through the LDS, each 8-byte word of the
     // [2][D][8] V pages that holds a block slot being read, merged and written
     // back whole after the barrier before the loop.  The stores have
     // completed before the barrier of step 1, and the block's pages are copied
@@ -387,12 +387,9 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
             for (int k = 0; k < SRC_STRIDE / 1024; ++k) {
                 const int ch = 64 * k + lane, u = ch / row16, t = 4 * tw + u;
                 const size_t off = ((((size_t)br * a.T_max + t) * a.Hkv + g) * D) * esz + 16 * (ch % row16);
-                // score wave v copies the K rows of its tokens, output wave
-                // 4 + v their V rows (before its page copies, so the wait
-                // for those covers them)
-                if (u < 4 && t < dl) {
-                    if (scorer) dma16_to_lds(static_cast<const uint8_t*>(a.k_src) + off, lds_base + src_k + 1024 * k);
-                    else dma16_to_lds(static_cast<const uint8_t*>(a.v_src) + off, lds_base + src_v + 1024 * k);
+                if (scorer && u < 4 && t < dl) {
+                    dma16_to_lds(static_cast<const uint8_t*>(a.k_src) + off, lds_base + src_k + 1024 * k);
+                    dma16_to_lds(static_cast<const uint8_t*>(a.v_src) + off, lds_base + src_v + 1024 * k);
                 }
             }
         }
@@ -432,62 +429,6 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         return *reinterpret_cast<const int*>(lds + C::ID_OFF + ((j & (kIdRing - 1)) * kPagesPerIter + c) * 4);
     };
     auto clamp_page = [&](int x) -> int { return min(max(__builtin_amdgcn_readfirstlane(x), 0), a.num_pages - 1); };
-    // the append mode: quantise this wave's four block rows (tokens 4 tw ..
-    // 4 tw + 3) from their LDS source copy exactly as the append quantises
-    // them.  K rows (score waves) go straight to the pool, D contiguous bytes
-    // each; V rows (output waves) go to the staging area, for the V words to be
-    // built after the barrier before the loop; the scales go to the staging
-    // area too.  A token of a page outside the pool is skipped.
-    auto quant_rows = [&](const bool is_v) {
-        const uint32_t src = is_v ? src_v : src_k;
-        float x[4][EQ];
-        if (a.src_bf16) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint16_t* px = reinterpret_cast<const uint16_t*>(lds + src + r * D * 2) + lane * EQ;
-#pragma unroll
-                for (int e = 0; e < EQ; ++e) x[r][e] = bit_cast<float>((uint32_t)px[e] << 16);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float* px = reinterpret_cast<const float*>(lds + src + r * D * 4) + lane * EQ;
-#pragma unroll
-                for (int e = 0; e < EQ; ++e) x[r][e] = px[e];
-            }
-        }
-        uint32_t q8[4];
-        uint16_t s8[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool in = 4 * tw + r < dl;
-#pragma unroll
-            for (int e = 0; e < EQ; ++e) x[r][e] = in ? x[r][e] : 0.0f;
-            q8[r] = quantize_row<D>(x[r], s8[r]);
-        }
-        int8_t* const kp = const_cast<int8_t*>(a.k_pool);     // writable in this mode
-        const int pA = (ctx - dl) / kPage;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * tw + r, pos = ctx - dl + t;
-            if (t >= dl) continue;
-            if (lane == 0) reinterpret_cast<uint16_t*>(lds + C::STG_S_OFF)[(is_v ? kPage : 0) + t] = s8[r];
-            if (!is_v) {
-                const int id = pos / kPage == pA ? idA : idB;
-                if (id >= 0 && id < a.num_pages) {
-                    int8_t* const kdst = kp + (((size_t)id * a.Hkv + g) * kPage + pos % kPage) * D + lane * EQ;
-                    if constexpr (EQ == 4) *reinterpret_cast<uint32_t*>(kdst) = q8[r];
-                    else if constexpr (EQ == 2) *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)q8[r];
-                    else *kdst = (int8_t)q8[r];
-                }
-            } else {
-                uint8_t* const row = lds + C::STG_OFF + t * D + lane * EQ;
-                if constexpr (EQ == 4) *reinterpret_cast<uint32_t*>(row) = q8[r];
-                else if constexpr (EQ == 2) *reinterpret_cast<uint16_t*>(row) = (uint16_t)q8[r];
-                else *row = (uint8_t)q8[r];
-            }
-        }
-    };
 
     if (!scorer) {
         int ids0 = 0;
@@ -509,22 +450,21 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
         } else {
             wait_vmcnt<0>();
         }
-        if constexpr (MASK == kMaskAppend)
-            if (blk) quant_rows(true);                        // this wave's V rows, into the staging area
     } else {
         wait_vmcnt<0>();
         if constexpr (MASK == kMaskAppend) {
             if (blk) {
-                // This wave's tokens: their K rows are quantised and stored
-                // now (the output waves quantise the V rows into the LDS
-                // staging area meanwhile).  The V words are built after the
-                // barrier: a V page is [2][D][8] (8-token groups, d-major),
-                // and single-byte stores scattered over it cost hundreds of
-                // cycles each, so every 8-byte word holding a block slot is
-                // read from the pool, merged and written back whole.  Those
-                // words are loaded first, so their latency overlaps the
-                // quantisation.  A token of a page outside this split, or a
-                // page id outside the pool, is skipped.
+                // This wave's tokens: K rows and V rows, each read from its
+                // LDS copy and quantised as the append quantises it.  K rows
+                // (D contiguous bytes) are stored now; V codes and all scales
+                // go to the LDS staging area, for the V words to be built
+                // after the barrier: a V page is [2][D][8] (8-token groups,
+                // d-major), and single-byte stores scattered over it cost
+                // hundreds of cycles each, so every 8-byte word holding a
+                // block slot is read from the pool, merged and written back
+                // whole.  Those words are loaded first, so their latency
+                // overlaps the quantisation.  A token of a page outside this
+                // split, or a page id outside the pool, is skipped.
                 const int sA = (ctx - dl) % kPage;            // the block's first slot in page pA
                 const int nvg = (sA + dl - 1) / 8 - sA / 8 + 1;   // 8-slot groups it touches (<= 3)
                 uint64_t* const word = vword;
@@ -537,7 +477,54 @@ __device__ __forceinline__ void partition_body(const VerifyArgs& a, uint8_t* lds
                         word[k] = *reinterpret_cast<const uint64_t*>(
                             a.v_pool + ((size_t)id * a.Hkv + g) * C::PAGE + ((vg & 1) * D + d) * 8);
                 }
-                quant_rows(false);
+                int8_t* const kp = const_cast<int8_t*>(a.k_pool);         // writable in this mode
+                const int pA = (ctx - dl) / kPage;
+                float x[8][EQ];
+                if (a.src_bf16) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const uint16_t* px = reinterpret_cast<const uint16_t*>(lds + (r < 4 ? src_k : src_v) + (r & 3) * D * 2) + lane * EQ;
+#pragma unroll
+                        for (int e = 0; e < EQ; ++e) x[r][e] = bit_cast<float>((uint32_t)px[e] << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const float* px = reinterpret_cast<const float*>(lds + (r < 4 ? src_k : src_v) + (r & 3) * D * 4) + lane * EQ;
+#pragma unroll
+                        for (int e = 0; e < EQ; ++e) x[r][e] = px[e];
+                    }
+                }
+                uint32_t q8[8];
+                uint16_t s8[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const bool in = 4 * tw + (r & 3) < dl;
+#pragma unroll
+                    for (int e = 0; e < EQ; ++e) x[r][e] = in ? x[r][e] : 0.0f;
+                    q8[r] = quantize_row<D>(x[r], s8[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int u = r & 3, t = 4 * tw + u, pos = ctx - dl + t;
+                    if (t >= dl) continue;
+                    if (lane == 0)
+                        reinterpret_cast<uint16_t*>(lds + C::STG_S_OFF)[(r < 4 ? 0 : kPage) + t] = s8[r];
+                    if (r < 4) {
+                        const int id = pos / kPage == pA ? idA : idB;
+                        if (id >= 0 && id < a.num_pages) {
+                            int8_t* const kdst = kp + (((size_t)id * a.Hkv + g) * kPage + pos % kPage) * D + lane * EQ;
+                            if constexpr (EQ == 4) *reinterpret_cast<uint32_t*>(kdst) = q8[r];
+                            else if constexpr (EQ == 2) *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)q8[r];
+                            else *kdst = (int8_t)q8[r];
+                        }
+                    } else {
+                        uint8_t* const row = lds + C::STG_OFF + t * D + lane * EQ;
+                        if constexpr (EQ == 4) *reinterpret_cast<uint32_t*>(row) = q8[r];
+                        else if constexpr (EQ == 2) *reinterpret_cast<uint16_t*>(row) = (uint16_t)q8[r];
+                        else *row = (uint8_t)q8[r];
+                    }
+                }
             }
         }
     }
